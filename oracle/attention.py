@@ -1,0 +1,260 @@
+"""Plain, slow, fp64 CPU oracle of exact scaled-dot-product attention.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+bench's CPU-baseline leg, never by the product path.  Shares no code with the
+HIP library.
+
+What is computed, and where the pages define it:
+
+* Forward — the standard (materialised) flow of "Flash Attention 是什么：2026
+  最新原理、架构演进与实战详解" (ai.lansai.wang), section 技术原理 › 核心工作机制:
+  scores S = Q·Kᵀ (here times the softmax scale, default 1/sqrt(d_k), and with
+  future keys masked when causal, both knobs of lqnn.cn "为什么Flash突然成了AI圈的
+  高频词" §3.3), a row softmax normalised by the row max and row sum, and the
+  weighted sum with V.  The row statistics are kept as the logsumexp
+  LSE = m + ln(l), the "max and sum" the same explainer says the forward keeps
+  for the backward (技术原理, 重计算 paragraph).
+* Backward — the gradient of the forward above, written out from its
+  definition (the pages only say the backward recomputes the local attention
+  from the saved statistics; 关键术语解析 §5 重计算).  The oracle recomputes
+  P from Q and K itself.
+* Paged decode — one query per sequence attending to all of that sequence's
+  cached keys, which live in fixed 256-token pages of a pool reserved up
+  front (0539edu.com "Flash不是那个被时代淘汰的插件" §2); a block table maps
+  the sequence's logical page b to a physical page.
+* online_forward — the tiled online-softmax recurrence of the explainer's
+  关键术语解析 §4 (在线 Softmax: the running max and normaliser update), with
+  the partial output rescaled alongside the normaliser and divided by the
+  final normaliser once (zwxr.cn §3.1).  Test-only: it exists to show the
+  online recurrence equals the two-pass definition; parity uses the
+  two-pass functions.
+
+Rows of queries may be processed in blocks (rows are independent); key
+blocks are never split in the two-pass functions.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+def _f64(x) -> np.ndarray:
+    """Upcast the exact stored values (fp32 or bf16, numpy or torch) to fp64."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.float64)
+
+
+def _scores(q_rows: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """S = scale · Q Kᵀ for a block of query rows ([r, d] x [n, d] -> [r, n])."""
+    return scale * (q_rows @ k.T)
+
+
+def _mask(s: np.ndarray, rows: np.ndarray, causal: bool) -> np.ndarray:
+    """Causal: query i sees keys 0..i only; every later key gets -inf."""
+    if causal:
+        cols = np.arange(s.shape[1])
+        s = np.where(cols[None, :] > rows[:, None], NEG_INF, s)
+    return s
+
+
+def _softmax_rows(s: np.ndarray):
+    """Two-pass row softmax: m = row max, E = exp(S - m), l = row sum, P = E / l.
+
+    A row with no visible key (all -inf) gives P = 0, l = 0 and m = -inf, so
+    its output is 0 and its logsumexp is -inf rather than NaN.
+    """
+    m = s.max(axis=1)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(s - m_safe[:, None])
+    l = e.sum(axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        p = np.where(l[:, None] > 0, e / np.where(l > 0, l, 1.0)[:, None], 0.0)
+        lse = np.where(l > 0, m_safe + np.log(np.where(l > 0, l, 1.0)), NEG_INF)
+    return p, lse
+
+
+def _dscores(p: np.ndarray, dp: np.ndarray) -> np.ndarray:
+    """dS = P ∘ (dP − D) with D_i = sum_j P_ij dP_ij (softmax Jacobian applied row-wise)."""
+    D = (p * dp).sum(axis=1)
+    return p * (dp - D[:, None])
+
+
+def _forward_head(q, k, v, causal, scale, rows=None, row_block=1024):
+    nq = q.shape[0]
+    rows = np.arange(nq) if rows is None else np.asarray(rows)
+    o = np.zeros((rows.size, v.shape[1]))
+    lse = np.zeros(rows.size)
+    for r0 in range(0, rows.size, row_block):
+        r = rows[r0:r0 + row_block]
+        s = _mask(_scores(q[r], k, scale), r, causal)
+        p, lse[r0:r0 + r.size] = _softmax_rows(s)
+        o[r0:r0 + r.size] = p @ v
+    return o, lse
+
+
+def _check(q, k, v, causal):
+    if q.shape[:-2] != k.shape[:-2] or k.shape != v.shape[:-1] + (k.shape[-1],):
+        raise ValueError("q, k, v must share leading dims; k and v share their key count")
+    if q.shape[-1] != k.shape[-1]:
+        raise ValueError("q and k need the same head dimension")
+    if causal and q.shape[-2] != k.shape[-2]:
+        raise ValueError("causal attention here takes as many queries as keys")
+
+
+def attention_forward(q, k, v, causal=False, scale=None, row_block=1024):
+    """O and LSE of exact attention for inputs of shape [..., N, d].
+
+    Returns (o [..., Nq, dv] fp64, lse [..., Nq] fp64) with LSE the natural
+    log of the row sum of exp(scaled, masked scores).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    _check(q, k, v, causal)
+    if scale is None:
+        scale = 1.0 / np.sqrt(q.shape[-1])
+    lead = q.shape[:-2]
+    heads = int(np.prod(lead))
+    qf = q.reshape((heads,) + q.shape[-2:])
+    kf = k.reshape((heads,) + k.shape[-2:])
+    vf = v.reshape((heads,) + v.shape[-2:])
+    o = np.zeros(qf.shape[:-1] + (vf.shape[-1],))
+    lse = np.zeros(qf.shape[:-1])
+    for h in range(qf.shape[0]):
+        o[h], lse[h] = _forward_head(qf[h], kf[h], vf[h], causal, scale, row_block=row_block)
+    return o.reshape(lead + o.shape[-2:]), lse.reshape(lead + lse.shape[-1:])
+
+
+def attention_forward_rows(q, k, v, rows, causal=False, scale=None):
+    """Forward for a subset of query rows of one head ([N, d] inputs).
+
+    Rows are independent in the definition, so a sample of rows is computed
+    exactly as the full forward would compute them.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    _check(q, k, v, causal)
+    if scale is None:
+        scale = 1.0 / np.sqrt(q.shape[-1])
+    return _forward_head(q, k, v, causal, scale, rows=np.asarray(rows))
+
+
+def attention_backward(q, k, v, dout, causal=False, scale=None, row_block=1024):
+    """dQ, dK, dV of L = sum(O * dO) for inputs of shape [..., N, d].
+
+    With P the softmax probabilities of the forward:
+      dV = Pᵀ dO;  dP = dO Vᵀ;  D_i = sum_j P_ij dP_ij;
+      dS = P ∘ (dP − D);  dQ = scale · dS K;  dK = scale · dSᵀ Q.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
+    _check(q, k, v, causal)
+    if scale is None:
+        scale = 1.0 / np.sqrt(q.shape[-1])
+    heads = int(np.prod(q.shape[:-2]))
+    qf, kf, vf, dof = (x.reshape((heads,) + x.shape[-2:]) for x in (q, k, v, do))
+    dq = np.zeros_like(qf)
+    dk = np.zeros_like(kf)
+    dv = np.zeros_like(vf)
+    for h in range(qf.shape[0]):
+        nq = qf.shape[1]
+        for r0 in range(0, nq, row_block):
+            r = np.arange(r0, min(nq, r0 + row_block))
+            s = _mask(_scores(qf[h, r], kf[h], scale), r, causal)
+            p, _ = _softmax_rows(s)
+            dv[h] += p.T @ dof[h, r]
+            dp = dof[h, r] @ vf[h].T
+            ds = _dscores(p, dp)
+            dq[h, r] = scale * (ds @ kf[h])
+            dk[h] += scale * (ds.T @ qf[h, r])
+    return dq.reshape(q.shape), dk.reshape(k.shape), dv.reshape(v.shape)
+
+
+def gather_pages(kv_pool, block_table, seq_len, seq, page_size):
+    """K and V of one sequence, token by token, through its block table.
+
+    Token t sits in logical page t // page_size, slot t % page_size; the
+    table row maps the logical page to a physical page of the pool, whose
+    layout is [pages, 2 (K, V), page_size, H, d].
+    """
+    H, d = kv_pool.shape[3], kv_pool.shape[4]
+    K = np.empty((seq_len, H, d))
+    V = np.empty((seq_len, H, d))
+    for t in range(seq_len):
+        page = int(block_table[seq, t // page_size])
+        slot = t % page_size
+        K[t] = kv_pool[page, 0, slot]
+        V[t] = kv_pool[page, 1, slot]
+    return K, V
+
+
+def decode_paged(q, kv_pool, block_table, seq_lens, scale=None, page_size=256):
+    """One query token per sequence over its paged KV cache.
+
+    q [S, H, d]; kv_pool [P, 2, page_size, H, d]; block_table [S, max_blocks];
+    seq_lens [S].  The query sees every one of the sequence's L_s cached keys
+    (its own key is already in the cache), so no causal mask applies.
+    Returns (o [S, H, d], lse [S, H]).
+    """
+    q, pool = _f64(q), _f64(kv_pool)
+    table = np.asarray(_f64(block_table), dtype=np.int64)
+    lens = np.asarray(_f64(seq_lens), dtype=np.int64)
+    S, H, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.zeros((S, H, d))
+    lse = np.zeros((S, H))
+    for s in range(S):
+        K, V = gather_pages(pool, table, int(lens[s]), s, page_size)
+        for h in range(H):
+            oh, lh = _forward_head(q[s, h][None, :], K[:, h], V[:, h], False, scale)
+            o[s, h], lse[s, h] = oh[0], lh[0]
+    return o, lse
+
+
+def online_forward(q, k, v, causal=False, scale=None, tile=16):
+    """Tiled single-pass forward with the online softmax (test-only).
+
+    Keys are visited in tiles of ``tile``.  Per query row a running max m and
+    normaliser l are kept; for each tile
+      m_new = max(m_old, max(x_tile)),
+      l_new = exp(m_old − m_new)·l_old + sum exp(x_tile − m_new),
+    and the unnormalised output is rescaled by the same exp(m_old − m_new)
+    before the tile's exp(x_tile − m_new)·V is added.  After the last tile the
+    output is divided by l once, and LSE = m + ln(l).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    _check(q, k, v, causal)
+    if scale is None:
+        scale = 1.0 / np.sqrt(q.shape[-1])
+    lead = q.shape[:-2]
+    heads = int(np.prod(lead))
+    qf, kf, vf = (x.reshape((heads,) + x.shape[-2:]) for x in (q, k, v))
+    nq, nk = qf.shape[1], kf.shape[1]
+    o = np.zeros(qf.shape[:-1] + (vf.shape[-1],))
+    lse = np.zeros(qf.shape[:-1])
+    rows = np.arange(nq)
+    for h in range(qf.shape[0]):
+        m = np.full(nq, NEG_INF)
+        l = np.zeros(nq)
+        acc = np.zeros((nq, vf.shape[-1]))
+        for j0 in range(0, nk, tile):
+            j1 = min(nk, j0 + tile)
+            x = scale * (qf[h] @ kf[h, j0:j1].T)
+            if causal:
+                cols = np.arange(j0, j1)
+                x = np.where(cols[None, :] > rows[:, None], NEG_INF, x)
+            m_new = np.maximum(m, x.max(axis=1))
+            live = np.isfinite(m_new)
+            m_ref = np.where(live, m_new, 0.0)
+            alpha = np.where(live, np.exp(np.where(live, m - m_ref, 0.0)), 1.0)
+            pt = np.exp(x - m_ref[:, None])
+            l = alpha * l + pt.sum(axis=1)
+            acc = alpha[:, None] * acc + pt @ vf[h, j0:j1]
+            m = m_new
+        with np.errstate(divide="ignore", invalid="ignore"):
+            o[h] = np.where(l[:, None] > 0, acc / np.where(l > 0, l, 1.0)[:, None], 0.0)
+            lse[h] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), NEG_INF)
+    return o.reshape(lead + o.shape[-2:]), lse.reshape(lead + lse.shape[-1:])

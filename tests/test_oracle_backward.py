@@ -1,0 +1,80 @@
+"""Pins of the fp64 oracle's backward: hand-worked values, finite differences,
+a library autograd and conservation invariants."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention_backward, attention_forward
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "handworked_attention.json")
+
+
+def _ev(expr):
+    return float(eval(expr, {"__builtins__": {}}, {"log": math.log}))
+
+
+def _mat(rows):
+    return np.array([[_ev(x) for x in r] for r in rows])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_handworked_backward(causal):
+    g = json.load(open(GOLDEN))
+    q, k, v, do = (_mat(g[x]) for x in ("q", "k", "v", "dout"))
+    dq, dk, dv = attention_backward(q, k, v, do, causal=causal, scale=g["scale"])
+    np.testing.assert_allclose(dq, _mat(g["backward"]["dq"]), atol=1e-13)
+    np.testing.assert_allclose(dk, _mat(g["backward"]["dk"]), atol=1e-13)
+    np.testing.assert_allclose(dv, _mat(g["backward"]["dv"]), atol=1e-13)
+
+
+def _loss(q, k, v, do, causal, scale):
+    o, _ = attention_forward(q, k, v, causal=causal, scale=scale)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 5, 16])
+def test_finite_differences(rng, causal, n):
+    d, scale, h = 4, 0.8, 1e-6
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    grads = attention_backward(q, k, v, do, causal=causal, scale=scale)
+    for which, g in zip(range(3), grads):
+        num = np.zeros_like(g)
+        for idx in np.ndindex(g.shape):
+            args_p = [q.copy(), k.copy(), v.copy()]
+            args_m = [q.copy(), k.copy(), v.copy()]
+            args_p[which][idx] += h
+            args_m[which][idx] -= h
+            num[idx] = (_loss(*args_p, do, causal, scale) - _loss(*args_m, do, causal, scale)) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_matches_torch_autograd_fp64(rng, causal):
+    B, H, n, d = 1, 2, 29, 8
+    scale = 1 / math.sqrt(d)
+    q, k, v, do = (rng.standard_normal((B, H, n, d)) for _ in range(4))
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+    o.backward(torch.from_numpy(do))
+    dq, dk, dv = attention_backward(q, k, v, do, causal=causal, scale=scale)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_conservation(rng, causal):
+    n, d = 40, 8
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    dq, dk, dv = attention_backward(q, k, v, do, causal=causal, scale=0.4, row_block=7)
+    # Each probability row sums to one, so the value gradients sum to dO's sum
+    # and the score gradients of a row sum to zero, hence sum_j dK_j = 0.
+    np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), atol=1e-12)
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-12)
+    if causal:
+        np.testing.assert_allclose(dq[0], 0.0, atol=1e-15)

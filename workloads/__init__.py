@@ -1,0 +1,155 @@
+"""Seeded synthetic inputs shared by the oracle tests, the GPU tests and the bench.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention arithmetic.  Every tensor is produced on the CPU with a
+``torch.Generator`` seeded explicitly, as fp32 N(0, 1) draws in a fixed order
+(Q, K, V, then dO, then the KV pool), and bf16 workloads round those draws to
+bf16 with round-to-nearest-even (``Tensor.to(torch.bfloat16)``) before either
+side sees them, so the oracle and the GPU consume the identical stored values.
+
+Workload shapes follow the pages' problem statement: Q/K/V laid out as
+[B, H, N, d] with the 16K-token example [1, 32, 16384, 128] ("为什么Flash突然成了AI圈的高频词",
+lqnn.cn, §2.1), the 32K context of the same page (§1), and a KV cache of
+fixed 256-token pages handed out from a pool reserved at load time
+(0539edu.com "Flash不是那个被时代淘汰的插件", §2).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+PAGE_SIZE = 256
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str            # "fwd" | "bwd" | "decode"
+    dtype: str           # "f32" | "bf16"
+    B: int = 1
+    H: int = 1
+    N: int = 1
+    d: int = 64
+    causal: bool = False
+    seed: int = 0
+    # decode only
+    num_seqs: int = 0
+    len_lo: int = 0
+    len_hi: int = 0
+    max_blocks: int = 0
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+# The configurations the hot path is specified on.  Seeds are fixed per config.
+CONFIGS = {
+    "c0": Workload("c0_fwd_f32_1x1x256x64", "fwd", "f32", 1, 1, 256, 64, False, 1000),
+    "c1": Workload("c1_fwd_causal_1x32x4096x128", "fwd", "bf16", 1, 32, 4096, 128, True, 1001),
+    "c2a": Workload("c2a_fwd_causal_1x32x16384x128", "fwd", "bf16", 1, 32, 16384, 128, True, 1002),
+    "c2b": Workload("c2b_fwd_causal_1x16x32768x128", "fwd", "bf16", 1, 16, 32768, 128, True, 1003),
+    "c2c": Workload("c2c_fwd_noncausal_1x32x16384x128", "fwd", "bf16", 1, 32, 16384, 128, False, 1004),
+    "c3": Workload("c3_bwd_causal_2x16x8192x128", "bwd", "bf16", 2, 16, 8192, 128, True, 1005),
+    "c4": Workload("c4_decode_paged_8seq_h32_d128", "decode", "bf16", H=32, d=128, seed=1006,
+                   num_seqs=8, len_lo=1024, len_hi=8192, max_blocks=32),
+}
+
+
+def _gen(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def _draw(g: torch.Generator, shape, dtype: str) -> torch.Tensor:
+    x = torch.randn(*shape, generator=g, dtype=torch.float32)
+    if dtype == "bf16":
+        return x.to(torch.bfloat16)
+    if dtype == "f32":
+        return x
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def attention_inputs(B, H, N, d, dtype="bf16", seed=0, with_dout=False):
+    """Q, K, V (and dO) of shape [B, H, N, d], CPU tensors of the given dtype."""
+    g = _gen(seed)
+    q = _draw(g, (B, H, N, d), dtype)
+    k = _draw(g, (B, H, N, d), dtype)
+    v = _draw(g, (B, H, N, d), dtype)
+    if not with_dout:
+        return q, k, v
+    do = _draw(g, (B, H, N, d), dtype)
+    return q, k, v, do
+
+
+@dataclass
+class PagedInputs:
+    q: torch.Tensor            # [S, H, d] bf16
+    kv_pool: torch.Tensor      # [P, 2, page, H, d] bf16
+    block_table: torch.Tensor  # [S, max_blocks] int32, -1 past the last page
+    seq_lens: torch.Tensor     # [S] int32
+    page_size: int
+    poisoned: bool
+
+
+def paged_inputs(num_seqs=8, H=32, d=128, len_lo=1024, len_hi=8192, max_blocks=32,
+                 seed=0, page_size=PAGE_SIZE, poison=False, spare_pages=0,
+                 seq_lens=None):
+    """Draw a paged KV cache.
+
+    Lengths are uniform integers in [len_lo, len_hi] (or given); each sequence
+    takes ceil(L/page) pages; the physical page ids are a random permutation of
+    the pool, handed to the sequences as consecutive slices, and unused table
+    entries hold -1.  With ``poison`` the slots past each sequence's length in
+    its last page are overwritten with a huge finite key and NaN values, and
+    ``spare_pages`` extra pages (never referenced by any table) hold NaN, so a
+    kernel that reads past a sequence's length cannot pass.
+    """
+    g = _gen(seed)
+    if seq_lens is None:
+        lens = torch.randint(len_lo, len_hi + 1, (num_seqs,), generator=g, dtype=torch.int64)
+    else:
+        lens = torch.as_tensor(seq_lens, dtype=torch.int64)
+        assert lens.numel() == num_seqs
+    pages = [(int(L) + page_size - 1) // page_size for L in lens]
+    if max(pages) > max_blocks:
+        raise ValueError("a sequence needs more pages than max_blocks")
+    used = sum(pages)
+    total = used + spare_pages
+    perm = torch.randperm(total, generator=g)
+    q = _draw(g, (num_seqs, H, d), "bf16")
+    pool = _draw(g, (total, 2, page_size, H, d), "bf16")
+    table = torch.full((num_seqs, max_blocks), -1, dtype=torch.int32)
+    off = 0
+    for s, p in enumerate(pages):
+        table[s, :p] = perm[off:off + p].to(torch.int32)
+        off += p
+    if poison:
+        for s, L in enumerate(lens.tolist()):
+            last = int(table[s, pages[s] - 1])
+            slot = L - (pages[s] - 1) * page_size
+            if slot < page_size:
+                pool[last, 0, slot:] = 3.0e4
+                pool[last, 1, slot:] = float("nan")
+        for p in perm[used:].tolist():
+            pool[p] = float("nan")
+    return PagedInputs(q, pool, table, lens.to(torch.int32), page_size, poison)
+
+
+def workload_inputs(w: Workload, **overrides):
+    """Inputs of a named configuration (optionally with overridden sizes)."""
+    if w.kind == "decode":
+        kw = dict(num_seqs=w.num_seqs, H=w.H, d=w.d, len_lo=w.len_lo, len_hi=w.len_hi,
+                  max_blocks=w.max_blocks, seed=w.seed)
+        kw.update(overrides)
+        return paged_inputs(**kw)
+    B = overrides.get("B", w.B)
+    H = overrides.get("H", w.H)
+    N = overrides.get("N", w.N)
+    d = overrides.get("d", w.d)
+    return attention_inputs(B, H, N, d, w.dtype, overrides.get("seed", w.seed),
+                            with_dout=(w.kind == "bwd"))
