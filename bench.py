@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+A step is one fused causal forward over [B=1, H=32, N=16384, d=128] bf16 (the
+pages' 16K-token example), inputs resident in HBM before the timed region.
+value = algorithmic attention TFLOP/s = 4·d·pairs·B·H / time, pairs = N(N+1)/2.
+The same JSON line also carries the other configurations of the hot path
+(32K and non-causal forward, the recomputing backward, paged decode in GB/s),
+the roofline of the dominant kernel and the CPU oracle timed on a bounded
+sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|bwd|decode]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s (fwd/bwd, % bf16 MFMA peak); paged-decode GB/s (% HBM peak)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+KERNEL_SOURCES = {          # sources a kernel's counters depend on
+    "fwd_bf16_kernel": ["exact_attention_fwd_amd/csrc/fa_fwd.hip", "exact_attention_fwd_amd/csrc/fa_device.h"],
+    "decode_split_kernel": ["exact_attention_fwd_amd/csrc/fa_decode.hip"],
+}
+
+
+def pairs(N, causal):
+    return N * (N + 1) // 2 if causal else N * N
+
+
+def fwd_flops(B, H, N, d, causal):
+    return 4.0 * d * pairs(N, causal) * B * H
+
+
+def bwd_flops(B, H, N, d, causal):
+    return 10.0 * d * pairs(N, causal) * B * H
+
+
+def decode_bytes(p):
+    S, H, d = p.q.shape
+    lens = p.seq_lens.tolist()
+    kv = sum(lens) * H * d * 2 * 2
+    pages = sum((L + p.page_size - 1) // p.page_size for L in lens)
+    return kv + S * H * d * 2 * 2 + S * H * 4 + pages * 4 + S * 4
+
+
+def src_hash(name):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[name]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(name, per_launch_units=1):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    the kernel's sources are unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(name)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("src_sha") != src_hash(name):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def timed_launches(fn, steps, warmup, flush=None):
+    """Per-launch HIP event timings on the current stream; returns (avg_ms, median_ms, total_ms)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        if flush is not None:
+            flush()
+        starts[i].record()
+        fn()
+        ends[i].record()
+    t1.record()
+    torch.cuda.synchronize()
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return sum(per) / len(per), statistics.median(per), t0.elapsed_time(t1)
+
+
+def bench_forward(cfg, steps, warmup):
+    import torch
+    import exact_attention_fwd_amd as fa
+    import workloads
+    w = workloads.CONFIGS[cfg]
+    q, k, v = (t.to("cuda:0") for t in workloads.workload_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
+    fn = lambda: fa.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+    avg, med, total = timed_launches(fn, steps, warmup)
+    fl = fwd_flops(w.B, w.H, w.N, w.d, w.causal)
+    del q, k, v, o, lse
+    return {"workload": w.name, "kernel": "fwd_bf16_kernel", "flops_per_launch": fl, "avg_ms": avg,
+            "median_ms": med, "total_ms": total, "tflops": fl / (avg * 1e-3) / 1e12,
+            "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
+def bench_backward(steps, warmup):
+    import torch
+    import exact_attention_fwd_amd as fa
+    import workloads
+    w = workloads.CONFIGS["c3"]
+    q, k, v, do = (t.to("cuda:0") for t in workloads.workload_inputs(w))
+    o, lse = fa.forward(q, k, v, causal=w.causal, scale=w.scale)
+    ws = torch.empty(fa.backward_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda:0")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fn = lambda: fa.backward(q, k, v, o, do, lse, causal=w.causal, scale=w.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
+    avg, med, total = timed_launches(fn, steps, warmup)
+    fl = bwd_flops(w.B, w.H, w.N, w.d, w.causal)
+    return {"workload": w.name, "kernels": "bwd_delta + bwd_dkdv + bwd_dq", "flops_per_call": fl, "avg_ms": avg,
+            "median_ms": med, "tflops": fl / (avg * 1e-3) / 1e12,
+            "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
+def bench_decode(steps, warmup):
+    import torch
+    import exact_attention_fwd_amd as fa
+    import workloads
+    w = workloads.CONFIGS["c4"]
+    p = workloads.workload_inputs(w)
+    q, pool, bt, sl = (t.to("cuda:0") for t in (p.q, p.kv_pool, p.block_table, p.seq_lens))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(fa.decode_workspace_bytes(*q.shape, bt.shape[1]), dtype=torch.uint8, device="cuda:0")
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")  # > the 256 MiB last-level cache
+    fn = lambda: fa.decode_paged(q, pool, bt, sl, scale=w.scale, workspace=ws, out=o, lse=lse)
+    avg, med, total = timed_launches(fn, steps, warmup, flush=lambda: scratch.fill_(1))
+    nbytes = decode_bytes(p)
+    return {"workload": w.name, "kernels": "decode_split + decode_merge", "bytes_per_call": nbytes,
+            "seq_lens": p.seq_lens.tolist(), "avg_ms": avg, "median_ms": med,
+            "gbs": nbytes / (med * 1e-3) / 1e9, "frac_of_peak": nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "cache": "1 GiB scratch written before every call (cold K/V)"}
+
+
+def cpu_baseline(budget_s=20.0):
+    """The fp64 oracle, as it stands, on whole heads of the 16K causal workload."""
+    import numpy as np
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    w = workloads.CONFIGS["c2a"]
+    q, k, v = workloads.workload_inputs(w)
+    qf, kf, vf = (x.reshape(w.B * w.H, w.N, w.d) for x in (q, k, v))
+    done, t_total = 0, 0.0
+    while done < w.B * w.H:
+        t0 = time.perf_counter()
+        oracle.attention_forward(qf[done], kf[done], vf[done], causal=True, scale=w.scale)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    fl = fwd_flops(1, 1, w.N, w.d, True) * done
+    return {"value": fl / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {w.B * w.H} heads of {w.name} (full causal forward per head, fp64 numpy), "
+                      f"{t_total:.1f} s; value = algorithmic flops of the sample / wall time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["fwd", "fwd32k", "fwdnc", "bwd", "decode"], default=None,
+                    help="run one path only (for profiler runs); prints its record")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    if args.only:
+        rec = {"fwd": lambda: bench_forward("c2a", args.steps, args.warmup),
+               "fwd32k": lambda: bench_forward("c2b", args.steps, args.warmup),
+               "fwdnc": lambda: bench_forward("c2c", args.steps, args.warmup),
+               "bwd": lambda: bench_backward(args.steps, args.warmup),
+               "decode": lambda: bench_decode(args.steps, args.warmup)}[args.only]()
+        print(json.dumps(rec), flush=True)
+        return
+
+    print("# forward c2a (headline)", file=sys.stderr, flush=True)
+    main_rec = bench_forward("c2a", args.steps, args.warmup)
+    secondary = []
+    for name, f in (("fwd c1", lambda: bench_forward("c1", args.steps, args.warmup)),
+                    ("fwd c2b", lambda: bench_forward("c2b", max(5, args.steps // 2), 2)),
+                    ("fwd c2c", lambda: bench_forward("c2c", max(5, args.steps // 2), 2)),
+                    ("bwd c3", lambda: bench_backward(max(5, args.steps // 2), 2)),
+                    ("decode c4", lambda: bench_decode(args.steps, args.warmup))):
+        print(f"# {name}", file=sys.stderr, flush=True)
+        secondary.append(f())
+        torch.cuda.empty_cache()
+    base = None
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        base = cpu_baseline()
+
+    fl = main_rec["flops_per_launch"]
+    achieved = fl / (main_rec["avg_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(main_rec["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_rec["total_ms"] / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q/K/V rounded to bf16",
+        "config": {"workload": main_rec["workload"], "B": 1, "H": 32, "N": 16384, "d": 128, "causal": True,
+                   "scale": 1 / math.sqrt(128)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for("fwd_bf16_kernel"),
+                     "kernel": "fwd_bf16_kernel", "avg_launch_ms": round(main_rec["avg_ms"], 4)},
+        "cpu_baseline": base,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

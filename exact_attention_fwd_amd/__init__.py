@@ -1,0 +1,172 @@
+"""Exact fused attention for AMD Instinct MI355X (gfx950).
+
+A thin binding over the C ABI of ``libfa.so`` (declared in include/fa.h):
+argument marshalling only.  Every step of forward, backward and paged decode
+runs in the library's HIP kernels; PyTorch supplies device memory and the
+current stream.  There is no fallback: if the library is missing or a call
+fails, a RuntimeError is raised.
+
+    o, lse = forward(q, k, v, causal=True)            # q,k,v [B,H,N,d] bf16/fp32
+    dq, dk, dv = backward(q, k, v, o, do, lse, causal=True)
+    o, lse = decode_paged(q, kv_pool, block_table, seq_lens)
+
+The softmax scale defaults to 1/sqrt(d), the default of the explainer pages
+(lqnn.cn "为什么Flash突然成了AI圈的高频词" §3.3).
+"""
+from __future__ import annotations
+
+import math
+
+from ._lib import (  # noqa: F401
+    FA_BF16,
+    FA_F32,
+    FaError,
+    lib,
+    library_path,
+    status_name,
+)
+
+__all__ = [
+    "forward",
+    "backward",
+    "decode_paged",
+    "backward_workspace_bytes",
+    "decode_workspace_bytes",
+    "FaError",
+    "lib",
+    "library_path",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _stream(t):
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check_dev(*ts):
+    dev = ts[0].device
+    for t in ts:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError("all tensors must live on the GPU")
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _call(rc):
+    if rc != 0:
+        raise FaError(rc)
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+            return_lse: bool = True):
+    """Fused forward; returns (o, lse) with lse fp32 [B, H, N] (or None)."""
+    torch = _torch()
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all have shape [B, H, N, d]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if not return_lse:
+        lse = None
+    _check_dev(q, k, v, o, lse)
+    with torch.cuda.device(q.device):
+        _call(lib().fa_forward(_dtype_code(q), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                               int(bool(causal)), float(scale), _stream(q)))
+    return o, lse
+
+
+def backward_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(lib().fa_backward_workspace_bytes(B, H, N, d))
+
+
+def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None, workspace=None,
+             dq=None, dk=None, dv=None):
+    """Recomputing backward; returns (dq, dk, dv) bf16 [B, H, N, d]."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    for t in (k, v, o, dout):
+        if t.shape != q.shape:
+            raise ValueError("q, k, v, o, dout must all have shape [B, H, N, d]")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32 [B, H, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = backward_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_dev(q, k, v, o, dout, lse, dq, dk, dv, workspace)
+    with torch.cuda.device(q.device):
+        _call(lib().fa_backward(_dtype_code(q), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), int(bool(causal)), float(scale),
+                                _stream(q)))
+    return dq, dk, dv
+
+
+def decode_workspace_bytes(num_seqs: int, H: int, d: int, max_blocks: int) -> int:
+    return int(lib().fa_decode_workspace_bytes(num_seqs, H, d, max_blocks))
+
+
+def decode_paged(q, kv_pool, block_table, seq_lens, scale: float | None = None, workspace=None, out=None,
+                 lse=None, return_lse: bool = True):
+    """Paged decode; q [S, H, d] bf16, kv_pool [P, 2, page, H, d] bf16,
+    block_table [S, max_blocks] int32, seq_lens [S] int32 (all on the GPU).
+    Returns (o [S, H, d] bf16, lse [S, H] fp32 or None)."""
+    torch = _torch()
+    S, H, d = q.shape
+    if kv_pool.dim() != 5 or kv_pool.shape[1] != 2 or kv_pool.shape[3] != H or kv_pool.shape[4] != d:
+        raise ValueError("kv_pool must be [pages, 2, page_size, H, d]")
+    if block_table.dim() != 2 or block_table.shape[0] != S or block_table.dtype != torch.int32:
+        raise ValueError("block_table must be int32 [S, max_blocks]")
+    if seq_lens.shape != (S,) or seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32 [S]")
+    if q.dtype != torch.bfloat16 or kv_pool.dtype != torch.bfloat16:
+        raise TypeError("paged decode takes bf16 q and kv_pool")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    P, _, page, _, _ = kv_pool.shape
+    mb = block_table.shape[1]
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((S, H), dtype=torch.float32, device=q.device)
+    if not return_lse:
+        lse = None
+    need = decode_workspace_bytes(S, H, d, mb)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_dev(q, kv_pool, block_table, seq_lens, o, lse, workspace)
+    with torch.cuda.device(q.device):
+        _call(lib().fa_decode_paged(S, H, d, page, P, mb, _ptr(q), _ptr(kv_pool), _ptr(block_table),
+                                    _ptr(seq_lens), _ptr(o), _ptr(lse), float(scale), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(q)))
+    return o, lse

@@ -1,0 +1,96 @@
+"""Build the gfx950 HIP library ``libfa.so`` in-tree with hipcc.
+
+    python -m exact_attention_fwd_amd.build        # or build() from Python
+
+Every .hip file under csrc/ is compiled for gfx950 only and linked into one
+shared library next to this file.  No JIT cache is used: the built library
+lives in the package directory, so it travels with the source tree.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(os.path.dirname(PKG_DIR), "include")
+LIB_NAME = "libfa.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Wno-unused-function",
+    # never emit packed fp32 VALU ops (v_pk_fma/add/mul_f32)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the gfx950 library cannot be built")
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile every kernel source and link libfa.so; returns its path."""
+    cc = hipcc()
+    srcs = sources()
+    if not srcs:
+        raise RuntimeError(f"no HIP sources under {CSRC}")
+    tmp = tempfile.mkdtemp(prefix="fa_build_")
+    try:
+        objs, procs = [], []
+        for src in srcs:
+            obj = os.path.join(tmp, os.path.basename(src) + ".o")
+            cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-c", src, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+            objs.append(obj)
+            if len(procs) >= jobs:
+                _wait(procs.pop(0), verbose)
+        for p in procs:
+            _wait(p, verbose)
+        out_tmp = LIB_PATH + ".tmp"
+        link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp,
+                "-Wl,-rpath,/opt/rocm/lib"]
+        if verbose:
+            print(" ".join(link), flush=True)
+        r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stdout}")
+        os.replace(out_tmp, LIB_PATH)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return LIB_PATH
+
+
+def _wait(item, verbose):
+    src, p = item
+    out, _ = p.communicate()
+    text = out.decode(errors="replace")
+    # hipcc's host pass does not know the packed-fp32 feature name; that note is harmless
+    lines = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln]
+    if p.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n" + "\n".join(lines))
+    if verbose and lines:
+        print("\n".join(lines), flush=True)
+
+
+if __name__ == "__main__":
+    path = build(verbose="-v" in sys.argv)
+    print(path)

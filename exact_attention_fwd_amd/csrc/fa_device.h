@@ -1,0 +1,186 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// Matrix products run on the CDNA4 bf16 MFMA v_mfma_f32_32x32x16_bf16
+// (fp32 accumulate).  Its register layout on a 64-lane wavefront, with
+// g = lane / 32 and n = lane % 32:
+//   A (32 x 16):  lane holds A[n][8g .. 8g+7]        (8 bf16, one 16-byte row piece)
+//   B (16 x 32):  lane holds B[8g .. 8g+7][n]
+//   C (32 x 32):  lane holds C[8(r/4) + 4g + r%4][n]  for r = 0..15
+// so a C tile is "one column per lane, 16 of its 32 rows per lane".
+//
+// Chaining two products (C of the first becomes the B operand of the second,
+// contracting over C's rows) needs C's row order to match B's k order.  The
+// first product therefore reads its A rows through perm_row(), which swaps
+// bits 2 and 3 of the row index: then register r of C in lane (g, n) holds
+// row 16(r/8) + 8g + r%8, and registers 8h..8h+7 of a lane are exactly the
+// B-operand k-slots 8g..8g+7 of the k-step covering rows 16h..16h+15.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit (v_exp_f32).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) on the transcendental unit (v_log_f32).
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Row permutation inside a 32-row MFMA block: swap bits 2 and 3 (an involution).
+__device__ __forceinline__ int perm_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// Combine a per-lane value with the one held by lane ^ 32 (v_permlane32_swap):
+// swapping x with itself leaves (x[l], x[l^32]) in the two results of lane l.
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Round two fp32 to bf16 (nearest-even, v_cvt_pk_bf16_f32) and pack them.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (bf16)lo;
+  v[1] = (bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float* p) {
+  u32x4 w;
+  w[0] = pack_bf16x2(p[0], p[1]);
+  w[1] = pack_bf16x2(p[2], p[3]);
+  w[2] = pack_bf16x2(p[4], p[5]);
+  w[3] = pack_bf16x2(p[6], p[7]);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// ---------------------------------------------------------------------------
+// LDS tiles of 64 rows.  Two layouts, both in 16-byte chunks XOR-swizzled so
+// that the operand reads of a wavefront are free of bank conflicts:
+//
+//  row-major  [64][D]   (row = token, D contiguous): chunk c of row r lives at
+//                       chunk c ^ rm_swz(r).  Operand reads take rows
+//                       perm_row(m) for lanes m = 0..15, and rm_swz() maps
+//                       those rows to 16 (D=128) / 8 (D=64) distinct chunks.
+//  transposed [D][64]   (row = feature, 64 tokens contiguous, 8 chunks of 8
+//                       tokens): chunk c of row d lives at c ^ tr_swz(d).
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int rm_swz(int r) {
+  return D >= 128 ? (perm_row(r) & 15) : (perm_row(r) & 7);
+}
+__device__ __forceinline__ int tr_swz(int d) { return (d ^ (d >> 3)) & 7; }
+
+constexpr int kTileRows = 64;
+
+// Row-major operand read: 8 consecutive features (16 bytes) of row r, chunk c.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_rm_read(const bf16* tile, int r, int c) {
+  return *reinterpret_cast<const bf16x8*>(tile + r * D + ((c ^ rm_swz<D>(r)) << 3));
+}
+// Transposed operand read: 8 consecutive tokens (chunk c) of feature row d.
+__device__ __forceinline__ bf16x8 lds_tr_read(const bf16* tile, int d, int c) {
+  return *reinterpret_cast<const bf16x8*>(tile + d * kTileRows + ((c ^ tr_swz(d)) << 3));
+}
+
+// Global rows [r0, r0+64) of a [rows, D] bf16 matrix into registers; rows at
+// or past `nrows` read as zero (never touched in memory).
+template <int D, int NT>
+struct RowTile {
+  static constexpr int kChunks = D / 8;
+  static constexpr int kPer = (kTileRows * kChunks + NT - 1) / NT;
+  u32x4 v[kPer];
+
+  __device__ __forceinline__ void load(const bf16* __restrict__ g, int r0, int nrows, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = tid + NT * i;
+      const int r = idx / kChunks, c = idx % kChunks;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (idx < kTileRows * kChunks && r0 + r < nrows)
+        x = *reinterpret_cast<const u32x4*>(g + (size_t)(r0 + r) * D + c * 8);
+      v[i] = x;
+    }
+  }
+  __device__ __forceinline__ void store(bf16* tile, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = tid + NT * i;
+      const int r = idx / kChunks, c = idx % kChunks;
+      if (idx < kTileRows * kChunks)
+        *reinterpret_cast<u32x4*>(tile + r * D + ((c ^ rm_swz<D>(r)) << 3)) = v[i];
+    }
+  }
+};
+
+// Same global rows, stored transposed ([D][64]).  Each work item takes four
+// consecutive rows of one 8-feature chunk and writes eight 4-token pieces.
+template <int D, int NT>
+struct TransTile {
+  static constexpr int kChunks = D / 8;
+  static constexpr int kItems = kChunks * (kTileRows / 4);
+  static constexpr int kPer = (kItems + NT - 1) / NT;
+  u32x4 v[kPer][4];
+
+  __device__ __forceinline__ void load(const bf16* __restrict__ g, int r0, int nrows, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int it = tid + NT * i;
+      const int c = it % kChunks, kg = it / kChunks;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = r0 + 4 * kg + j;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (it < kItems && r < nrows) x = *reinterpret_cast<const u32x4*>(g + (size_t)r * D + c * 8);
+        v[i][j] = x;
+      }
+    }
+  }
+  __device__ __forceinline__ void store(bf16* tile, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int it = tid + NT * i;
+      if (it >= kItems) continue;
+      const int c = it % kChunks, kg = it / kChunks;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t a0 = v[i][0][w], a1 = v[i][1][w], a2 = v[i][2][w], a3 = v[i][3][w];
+        // feature 8c+2w: low halves of the four rows; feature 8c+2w+1: high halves
+        u32x2 lo, hi;
+        lo[0] = (a0 & 0xffffu) | (a1 << 16);
+        lo[1] = (a2 & 0xffffu) | (a3 << 16);
+        hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
+        hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+        const int d0 = 8 * c + 2 * w, d1 = d0 + 1;
+        *reinterpret_cast<u32x2*>(tile + d0 * kTileRows + (((kg >> 1) ^ tr_swz(d0)) << 3) + ((kg & 1) << 2)) = lo;
+        *reinterpret_cast<u32x2*>(tile + d1 * kTileRows + (((kg >> 1) ^ tr_swz(d1)) << 3) + ((kg & 1) << 2)) = hi;
+      }
+    }
+  }
+};
+
+// Key (or query) offset inside a 64-row tile of register r of C block kb, for
+// a lane in half g, when the A rows of the product were read via perm_row().
+__device__ __forceinline__ int crow(int kb, int r, int g) { return 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7); }
+
+}  // namespace fa

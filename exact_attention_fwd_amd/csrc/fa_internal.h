@@ -1,0 +1,62 @@
+// Internal launch interface between the C ABI (fa_api.hip) and the kernel
+// translation units.  Arguments reaching these functions are validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct ForwardArgs {
+  bool bf16;
+  int BH, N, d;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int causal;
+  float scale;
+  hipStream_t stream;
+};
+
+struct BackwardArgs {
+  int BH, N, d;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // [BH, N] workspace
+  int causal;
+  float scale;
+  hipStream_t stream;
+};
+
+struct DecodeArgs {
+  int S, H, d, page_size, max_blocks;
+  const void* q;
+  const void* kv_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* o;
+  float* lse;
+  float scale;
+  float* part;  // [S, H, max_blocks, d + 2] fp32 workspace
+  hipStream_t stream;
+};
+
+hipError_t launch_forward(const ForwardArgs& a);
+hipError_t launch_backward(const BackwardArgs& a);
+hipError_t launch_decode(const DecodeArgs& a);
+
+// Workspace sizes (bytes, rounded up to 256).
+size_t backward_workspace_bytes(long long BH, long long N);
+size_t decode_workspace_bytes(long long S, long long H, long long d, long long max_blocks);
+
+}  // namespace fa

@@ -1,0 +1,164 @@
+/*
+ * fa.h — C ABI of the exact-attention library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention as one fused, tiled
+ * pass per query tile: score tiles Q·Kᵀ, the softmax and the product with V
+ * never leave the compute unit, the running row max m and normaliser l of the
+ * online softmax rescale the partial output, and only O and the per-row
+ * logsumexp reach device memory.  Sources of the definition:
+ *   - "Flash Attention 是什么：2026 最新原理、架构演进与实战详解" (ai.lansai.wang):
+ *     技术原理 › 核心工作机制 (standard flow S = Q·Kᵀ, softmax, ·V; tiling;
+ *     online softmax; recomputation from the saved max and sum);
+ *     关键术语解析 §4 (the m and l update equations); 常见误解澄清, 误解一
+ *     (the result is exact; only rounding order differs).
+ *   - lqnn.cn "为什么Flash突然成了AI圈的高频词" §2.1 (Q/K/V as [B, H, N, d],
+ *     e.g. [1, 32, 16384, 128]) and §3.3 (causal flag; softmax scale with
+ *     default 1/sqrt(d_k)).
+ *   - 0539edu.com "Flash不是那个被时代淘汰的插件" §2 (a KV page pool reserved
+ *     at load time, fixed 256-token pages handed to sequences; decode is
+ *     memory-bound, prefill compute-bound).
+ *
+ * Conventions for every entry point
+ *   - Tensors are dense, row-major and contiguous, innermost dimension last.
+ *   - Every data pointer is a DEVICE pointer owned by the caller; the library
+ *     never allocates, frees or keeps a pointer after returning.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously on it; the library never synchronises.
+ *   - Arguments are validated on the host BEFORE anything is launched; on a
+ *     validation error nothing is enqueued and the output buffers are left
+ *     untouched.  A failed launch returns FA_ERR_HIP.
+ *   - Contents of device-resident index arrays (block tables, lengths) cannot
+ *     be checked without a synchronisation and are trusted: out-of-range
+ *     values are undefined behaviour.
+ *   - Calls on one stream are ordered; calls that share output or workspace
+ *     buffers on different streams race.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL_PTR = 1,     /* a required pointer is NULL                              */
+  FA_ERR_BAD_SHAPE = 2,    /* a size is negative/zero where it may not be, or overflows */
+  FA_ERR_UNSUPPORTED = 3,  /* head dim, dtype or page size this build does not handle  */
+  FA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than *_workspace_bytes()       */
+  FA_ERR_HIP = 5           /* the HIP runtime reported an error (no device, launch)    */
+} fa_status;
+
+typedef enum {
+  FA_F32 = 0,              /* IEEE fp32 in and out, fp32 arithmetic                     */
+  FA_BF16 = 1              /* bf16 in and out, bf16 matrix products accumulated in fp32 */
+} fa_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fa_status_str(fa_status s);
+
+/* Text of the last HIP runtime error seen by this thread's calls into the
+ * library (static string, never NULL; "no error" if none). */
+const char* fa_last_hip_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fa_version(void);
+
+/*
+ * fa_forward — O = softmax(scale · Q Kᵀ [+ causal mask]) V and the row logsumexp.
+ *
+ *   dt      FA_BF16 (head dim 64 or 128) or FA_F32 (head dim 64 or 128).
+ *   B,H,N,d batch, heads, sequence length (queries = keys = N), head dim.
+ *           B, H >= 1; N >= 0 (N == 0 is a no-op returning FA_OK).
+ *   q,k,v   [B, H, N, d] of dtype dt.
+ *   o       [B, H, N, d] of dtype dt (written).  bf16 outputs are rounded to
+ *           nearest-even from the fp32 result.
+ *   lse     [B, H, N] fp32 (written) or NULL to skip: the natural log of the
+ *           sum over visible keys of exp(scale · q_i·k_j).  It is the only
+ *           statistic a recomputing backward needs.
+ *   causal  non-zero: query i sees keys 0..i (future keys masked).
+ *   scale   softmax scale; callers wanting the usual default pass 1/sqrt(d).
+ *           Must be finite.
+ * Work: 4·d·pairs·B·H flops, pairs = N(N+1)/2 causal, N² otherwise; extra
+ * device memory: none (no N×N buffer).
+ */
+fa_status fa_forward(fa_dtype dt, int B, int H, int N, int d,
+                     const void* q, const void* k, const void* v,
+                     void* o, float* lse, int causal, float scale, void* stream);
+
+/*
+ * Workspace the backward needs, in bytes: one fp32 per query row (the row
+ * dot product D_i = dO_i · O_i), rounded up to 256 bytes.  O(B·H·N); no N×N.
+ */
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * fa_backward — gradients of L = Σ O∘dO through the forward above, with the
+ * attention probabilities recomputed tile by tile from Q, K and the saved
+ * logsumexp instead of being stored (the explainer's recomputation).
+ *
+ *   dt            FA_BF16 only; head dim 64 or 128.
+ *   q,k,v         forward inputs [B, H, N, d] bf16.
+ *   o, dout       forward output and its gradient [B, H, N, d] bf16.
+ *   lse           [B, H, N] fp32 as written by fa_forward on the same inputs.
+ *   dq,dk,dv      [B, H, N, d] bf16 (written), fp32-accumulated, rounded
+ *                 to nearest-even.
+ *   workspace     device buffer of >= fa_backward_workspace_bytes() bytes,
+ *                 owned by the caller; contents on entry are ignored.
+ *   causal, scale as in fa_forward.
+ * Deterministic: every output element is accumulated in a fixed order.
+ */
+fa_status fa_backward(fa_dtype dt, int B, int H, int N, int d,
+                      const void* q, const void* k, const void* v,
+                      const void* o, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes,
+                      int causal, float scale, void* stream);
+
+/*
+ * Workspace for fa_decode_paged in bytes: per (sequence, head, KV split) a
+ * partial running max, normaliser and unnormalised output row in fp32, with
+ * at most max_blocks_per_seq splits per sequence.
+ */
+size_t fa_decode_workspace_bytes(int num_seqs, int H, int d, int max_blocks_per_seq);
+
+/*
+ * fa_decode_paged — one new query token per sequence against that sequence's
+ * paged KV cache (split over pages, then merged exactly through the running
+ * max / normaliser algebra of the online softmax).
+ *
+ *   num_seqs,H,d        sequences (>= 1), heads (>= 1), head dim (128 or 64).
+ *   page_size           tokens per page; this build supports 256.
+ *   num_pages           pages in the pool (>= 1).
+ *   max_blocks_per_seq  columns of block_table (>= 1).
+ *   q                   [num_seqs, H, d] bf16.
+ *   kv_pool             [num_pages, 2, page_size, H, d] bf16; index 0 of the
+ *                       second dim holds K, index 1 holds V.
+ *   block_table         [num_seqs, max_blocks_per_seq] int32 (device): entry
+ *                       b of row s is the physical page holding tokens
+ *                       b·page_size .. b·page_size+page_size-1 of sequence s.
+ *                       Entries past ceil(L_s/page_size) are never read.
+ *   seq_lens            [num_seqs] int32 (device), 1 <= L_s <=
+ *                       max_blocks_per_seq·page_size.  Slots >= L_s in the
+ *                       last page are never read.
+ *   o                   [num_seqs, H, d] bf16 (written).
+ *   lse                 [num_seqs, H] fp32 (written) or NULL.
+ *   scale               softmax scale (finite).
+ *   workspace           >= fa_decode_workspace_bytes() bytes, caller-owned.
+ * The query sees all L_s cached keys (no causal mask).  Deterministic.
+ */
+fa_status fa_decode_paged(int num_seqs, int H, int d, int page_size,
+                          int num_pages, int max_blocks_per_seq,
+                          const void* q, const void* kv_pool,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          void* o, float* lse, float scale,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,223 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle on
+the same seeded inputs.
+
+Small shapes are compared element by element over every output; the full
+configurations (16K and 32K forward, the 8K backward) are run on the GPU at
+full size, in the launch configuration the bench times, and compared on
+whole heads plus sampled rows that the oracle computes one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.parity import BF16_MAX, BF16_MEAN, F32_MAX, LSE_MAX, check, to64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X")
+    import exact_attention_fwd_amd as fa  # noqa: F401  (fails loudly if libfa.so is missing)
+    assert "gfx950" in torch.cuda.get_device_properties(0).gcnArchName
+    yield
+
+
+def fa():
+    import exact_attention_fwd_amd
+    return exact_attention_fwd_amd
+
+
+def cuda(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+def _fwd_compare(name, q, k, v, causal, scale, heads=None, rows=None, f32=False):
+    """Run the GPU forward on full inputs; compare selected heads fully and
+    (optionally) sampled rows of other heads."""
+    qd, kd, vd = cuda(q, k, v)
+    o, lse = fa().forward(qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    B, H, N, d = q.shape
+    qf, kf, vf = (x.reshape(B * H, N, d) for x in (q, k, v))
+    of, lf = o.reshape(B * H, N, d), lse.reshape(B * H, N)
+    heads = range(B * H) if heads is None else heads
+    got_o, ref_o, got_l, ref_l = [], [], [], []
+    for h in heads:
+        ro, rl = oracle.attention_forward(qf[h], kf[h], vf[h], causal=causal, scale=scale)
+        got_o.append(to64(of[h])), ref_o.append(ro), got_l.append(to64(lf[h])), ref_l.append(rl)
+    if rows:
+        for h, rr in rows.items():
+            ro, rl = oracle.attention_forward_rows(qf[h], kf[h], vf[h], rr, causal=causal, scale=scale)
+            got_o.append(to64(of[h][rr])), ref_o.append(ro), got_l.append(to64(lf[h][rr])), ref_l.append(rl)
+    go, ro = np.concatenate([x.ravel() for x in got_o]), np.concatenate([x.ravel() for x in ref_o])
+    gl, rl = np.concatenate([x.ravel() for x in got_l]), np.concatenate([x.ravel() for x in ref_l])
+    if f32:
+        check(f"{name} O", go, ro, F32_MAX)
+    else:
+        check(f"{name} O", go, ro, BF16_MAX, BF16_MEAN)
+    check(f"{name} LSE", gl, rl, LSE_MAX)
+
+
+def test_c0_fp32_forward():
+    w = workloads.CONFIGS["c0"]
+    q, k, v = workloads.workload_inputs(w)
+    _fwd_compare("c0", q, k, v, w.causal, w.scale, f32=True)
+
+
+def test_c1_causal_forward_all_heads():
+    w = workloads.CONFIGS["c1"]
+    q, k, v = workloads.workload_inputs(w)
+    _fwd_compare("c1", q, k, v, w.causal, w.scale)
+
+
+def _sample_rows(N, seed, count=48):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 63, 64, 127, 128, 129, N // 2, N - 129, N - 128, N - 65, N - 64, N - 2, N - 1]
+    return sorted(set([r for r in fixed if 0 <= r < N] + rng.integers(0, N, count).tolist()))
+
+
+@pytest.mark.parametrize("cfg", ["c2a", "c2b", "c2c"])
+def test_c2_long_forward_full_size(cfg):
+    w = workloads.CONFIGS[cfg]
+    print(f"[{cfg}] generating {w.B}x{w.H}x{w.N}x{w.d}", flush=True)
+    q, k, v = workloads.workload_inputs(w)
+    BH = w.B * w.H
+    full = [0] if cfg == "c2b" else [0, BH - 1]
+    rows = {h: _sample_rows(w.N, 17 + h) for h in (1, BH // 2, BH - 2)}
+    _fwd_compare(cfg, q, k, v, w.causal, w.scale, heads=full, rows=rows)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 7, 63, 64, 100, 129, 255, 257, 1000])
+def test_odd_lengths_bf16(N, causal, d):
+    q, k, v = workloads.attention_inputs(1, 3, N, d, "bf16", seed=N * 7 + d + int(causal))
+    _fwd_compare(f"bf16 N={N} d={d} causal={causal}", q, k, v, causal, 1 / math.sqrt(d))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 33, 200])
+def test_odd_lengths_fp32(N, d):
+    for causal in (False, True):
+        q, k, v = workloads.attention_inputs(2, 1, N, d, "f32", seed=N + d)
+        _fwd_compare(f"f32 N={N} d={d} causal={causal}", q, k, v, causal, 1 / math.sqrt(d), f32=True)
+
+
+def test_batch_and_explicit_scale():
+    q, k, v = workloads.attention_inputs(3, 5, 300, 128, "bf16", seed=99)
+    _fwd_compare("B=3 H=5 scale=0.3", q, k, v, True, 0.3)
+    qd, kd, vd = cuda(q, k, v)
+    a = fa().forward(qd, kd, vd, causal=False)
+    b = fa().forward(qd, kd, vd, causal=False, scale=1 / math.sqrt(128))
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_forward_is_deterministic_and_n0_is_noop():
+    q, k, v = cuda(*workloads.attention_inputs(1, 8, 2000, 128, "bf16", seed=5))
+    a = fa().forward(q, k, v, causal=True)
+    b = fa().forward(q, k, v, causal=True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    z = torch.zeros(1, 2, 0, 128, dtype=torch.bfloat16, device=DEV)
+    o, lse = fa().forward(z, z, z, causal=True)
+    assert o.shape == z.shape and lse.shape == (1, 2, 0)
+
+
+# ------------------------------------------------------------------ backward
+def _bwd_compare(name, q, k, v, do, causal, scale, heads=None):
+    qd, kd, vd, dod = cuda(q, k, v, do)
+    o, lse = fa().forward(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv = fa().backward(qd, kd, vd, o, dod, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    B, H, N, d = q.shape
+    flat = lambda x: x.reshape(B * H, N, d)
+    heads = range(B * H) if heads is None else heads
+    got = {n: [] for n in ("dq", "dk", "dv")}
+    ref = {n: [] for n in ("dq", "dk", "dv")}
+    for h in heads:
+        r = oracle.attention_backward(flat(q)[h], flat(k)[h], flat(v)[h], flat(do)[h], causal=causal, scale=scale)
+        for n_, g_, r_ in zip(("dq", "dk", "dv"), (dq, dk, dv), r):
+            got[n_].append(to64(flat(g_.cpu())[h]).ravel())
+            ref[n_].append(r_.ravel())
+    for n_ in ("dq", "dk", "dv"):
+        check(f"{name} {n_}", np.concatenate(got[n_]), np.concatenate(ref[n_]), BF16_MAX, BF16_MEAN)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 7, 100, 257, 700])
+def test_backward_small(N, causal, d):
+    q, k, v, do = workloads.attention_inputs(1, 2, N, d, "bf16", seed=3 * N + d, with_dout=True)
+    _bwd_compare(f"bwd N={N} d={d} causal={causal}", q, k, v, do, causal, 1 / math.sqrt(d))
+
+
+def test_c3_backward_full_size():
+    w = workloads.CONFIGS["c3"]
+    print(f"[c3] generating {w.B}x{w.H}x{w.N}x{w.d}", flush=True)
+    q, k, v, do = workloads.workload_inputs(w)
+    _bwd_compare("c3", q, k, v, do, w.causal, w.scale, heads=[0, w.B * w.H - 1])
+
+
+def test_backward_is_deterministic():
+    q, k, v, do = cuda(*workloads.attention_inputs(1, 4, 1500, 128, "bf16", seed=8, with_dout=True))
+    o, lse = fa().forward(q, k, v, causal=True)
+    a = fa().backward(q, k, v, o, do, lse, causal=True)
+    b = fa().backward(q, k, v, o, do, lse, causal=True)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+# -------------------------------------------------------------------- decode
+def _decode_compare(name, p, scale=None):
+    d = p.q.shape[-1]
+    scale = 1 / math.sqrt(d) if scale is None else scale
+    qd, pool, bt, sl = cuda(p.q, p.kv_pool, p.block_table, p.seq_lens)
+    o, lse = fa().decode_paged(qd, pool, bt, sl, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_paged(p.q, p.kv_pool, p.block_table, p.seq_lens, scale=scale, page_size=p.page_size)
+    check(f"{name} O", to64(o.cpu()), ro, BF16_MAX, BF16_MEAN)
+    check(f"{name} LSE", to64(lse.cpu()), rl, LSE_MAX)
+    return o, lse
+
+
+def test_c4_decode_full():
+    w = workloads.CONFIGS["c4"]
+    _decode_compare("c4", workloads.workload_inputs(w))
+
+
+def test_c4_decode_poisoned_tails_and_spare_pages():
+    w = workloads.CONFIGS["c4"]
+    p = workloads.workload_inputs(w, poison=True, spare_pages=16)
+    o, _ = _decode_compare("c4 poisoned", p)
+    assert torch.isfinite(o.float()).all()
+
+
+@pytest.mark.parametrize("H,d", [(12, 128), (8, 64), (3, 64)])
+def test_decode_shapes(H, d):
+    lens = [1, 255, 256, 257, 1000, 2048]
+    p = workloads.paged_inputs(num_seqs=len(lens), H=H, d=d, max_blocks=9, seed=H + d, seq_lens=lens,
+                               poison=True, spare_pages=3)
+    _decode_compare(f"decode H={H} d={d}", p)
+
+
+def test_decode_is_deterministic():
+    p = workloads.paged_inputs(num_seqs=4, H=32, d=128, len_lo=300, len_hi=3000, max_blocks=12, seed=4)
+    args = cuda(p.q, p.kv_pool, p.block_table, p.seq_lens)
+    a = fa().decode_paged(*args)
+    b = fa().decode_paged(*args)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_errors_raise():
+    x = torch.zeros(1, 1, 8, 128, dtype=torch.float32, device=DEV)
+    lse = torch.zeros(1, 1, 8, dtype=torch.float32, device=DEV)
+    with pytest.raises(fa().FaError):
+        fa().backward(x, x, x, x, x, lse)  # fp32 backward is not provided
