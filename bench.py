@@ -153,6 +153,17 @@ def bench_decode(steps, warmup):
             "cache": "1 GiB scratch written before every call (cold K/V)"}
 
 
+def bench_copy(steps, warmup):
+    """A plain 1 GiB device-to-device copy: calibrates the HBM byte counters."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    avg, med, total = timed_launches(lambda: dst.copy_(src), steps, warmup)
+    return {"workload": "copy_1GiB", "bytes_read": n, "bytes_written": n, "avg_ms": avg,
+            "gbs": 2 * n / (avg * 1e-3) / 1e9}
+
+
 def cpu_baseline(budget_s=20.0):
     """The fp64 oracle, as it stands, on whole heads of the 16K causal workload."""
     import numpy as np
@@ -185,7 +196,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["fwd", "fwd32k", "fwdnc", "bwd", "decode"], default=None,
+    ap.add_argument("--only", choices=["fwd", "fwd32k", "fwdnc", "fwd4k", "bwd", "decode", "copy"], default=None,
                     help="run one path only (for profiler runs); prints its record")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -203,7 +214,9 @@ def main():
         rec = {"fwd": lambda: bench_forward("c2a", args.steps, args.warmup),
                "fwd32k": lambda: bench_forward("c2b", args.steps, args.warmup),
                "fwdnc": lambda: bench_forward("c2c", args.steps, args.warmup),
+               "fwd4k": lambda: bench_forward("c1", args.steps, args.warmup),
                "bwd": lambda: bench_backward(args.steps, args.warmup),
+               "copy": lambda: bench_copy(args.steps, args.warmup),
                "decode": lambda: bench_decode(args.steps, args.warmup)}[args.only]()
         print(json.dumps(rec), flush=True)
         return

@@ -179,6 +179,45 @@ struct TransTile {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Buffer resources: 128-bit descriptors over one contiguous byte range.  Raw
+// buffer loads past `bytes` return zeros in hardware, so tile loads need no
+// bounds branches.  (Word 3 = 0x00020000 is the CDNA data-format word for raw
+// 32-bit access.)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+// Direct HBM -> LDS load of 16 bytes per lane: lane l's bytes land at
+// lds_wave_base + 16*l (the destination is one contiguous 1 KiB block per
+// wavefront instruction); `off` is this lane's byte offset in the buffer.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, (int)off, 0, 0, 0);
+}
+// Wait until every direct-to-LDS load this wavefront issued has landed.
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i & 3) of the 4-element pieces addressed by lanes 4t + (i >> 2), t = 0..3.
+// If lane j of the group addresses row (r0 + j/4), columns c0 + 4(j%4) ..+3 of
+// a row-major tile, lane i receives rows r0..r0+3 of column c0 + i.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
+}
+
+// Sum of a packed pair of bf16 added to an fp32 accumulator (v_dot2_f32_bf16).
+__device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
+}
+
 // Key (or query) offset inside a 64-row tile of register r of C block kb, for
 // a lane in half g, when the A rows of the product were read via perm_row().
 __device__ __forceinline__ int crow(int kb, int r, int g) { return 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7); }

@@ -51,14 +51,29 @@ __device__ __forceinline__ void map_block(int bid, int nqb, int BH, bool causal,
   bh = head;
 }
 
+// Swizzle of the row-major V tile: the transposed operand reads take four
+// consecutive rows per 16-lane group, so rows r..r+3 get their 32-byte column
+// pieces moved to four different 32-byte bank windows.
+__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 1; }
+
+// Rescale the output only when the running max grows by more than this many
+// powers of two.  Between rescales p = 2^(s·scale·log2e − m) <= 2^8: the
+// output, its normaliser and the logsumexp all use the same reference m, so
+// the result is the same exact quantity (only rounding differs).
+constexpr float kRescaleThreshold = 8.0f;
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, float scale_log2) {
   constexpr int KSTEPS = D / 16;  // MFMA k-steps over the head dim
   constexpr int DBLK = D / 32;    // 32-row output blocks over the head dim
-  __shared__ __attribute__((aligned(16))) bf16 sK[kTileRows * D];
-  __shared__ __attribute__((aligned(16))) bf16 sVt[D * kTileRows];
+  constexpr int TILE = kTileRows * D;
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int ROWS_PER_DMA = 64 / CPR;      // rows per 1 KiB wavefront load
+  constexpr int DMA_PER_WAVE = kTileRows / ROWS_PER_DMA / kWaves;
+  // [stage][K, V][64][D], both row-major; two stages form a load/compute ring
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * 2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -68,21 +83,49 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   map_block(blockIdx.x, nqb, BH, CAUSAL, qb, bh);
 
   const size_t head_off = (size_t)bh * N * D;
-  const bf16* Qh = Q + head_off;
-  const bf16* Kh = K + head_off;
-  const bf16* Vh = V + head_off;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto rq = make_rsrc(Q + head_off, head_bytes);
+  const auto rk = make_rsrc(K + head_off, head_bytes);
+  const auto rv = make_rsrc(V + head_off, head_bytes);
   const int q0 = qb * kBR;
   const int qw = q0 + wave * 32;
   const int qrow = qw + n;  // this lane's query
   const bool wave_live = qw < N;
 
-  // Qᵀ as the B operand: lane (g, n) holds Q[qrow][16kk + 8g .. +7].
+  // Qᵀ as the B operand: lane (g, n) holds Q[qrow][16kk + 8g .. +7] (zeros past N).
   bf16x8 qreg[KSTEPS];
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (qrow < N) x = *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + 16 * kk + 8 * g);
-    qreg[kk] = __builtin_bit_cast(bf16x8, x);
+  for (int kk = 0; kk < KSTEPS; ++kk)
+    qreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)qrow * (D * 2) + (16 * kk + 8 * g) * 2));
+
+  // Direct-to-LDS loads of tile t into stage st: wave w fills 1 KiB blocks
+  // w*DMA_PER_WAVE .. of both tiles; lane l writes physical chunk l % CPR of
+  // row l / CPR of its block, fetching the logical chunk that swizzles there.
+  const int dma_row = lane / CPR, dma_pc = lane % CPR;
+  auto issue = [&](int t, int st) {
+    bf16* ks = smem + st * 2 * TILE;
+    bf16* vs = ks + TILE;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      const int blk = wave * DMA_PER_WAVE + i;
+      const int row = blk * ROWS_PER_DMA + dma_row;
+      const uint32_t roff = (uint32_t)(t * kTileRows + row) * (D * 2);
+      lds_dma16(rk, ks + blk * 512, roff + ((dma_pc ^ rm_swz<D>(row)) << 4));
+      lds_dma16(rv, vs + blk * 512, roff + ((dma_pc ^ v_swz(row)) << 4));
+    }
+  };
+
+  // Per-lane LDS element offsets of the operand reads (loop invariant).
+  int koff[KSTEPS];  // K rows perm_row(n) (+32 for the second block), chunk 2kk+g
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) koff[kk] = perm_row(n) * D + (((2 * kk + g) ^ (n & (CPR - 1))) << 3);
+  const int G = lane >> 4, j16 = lane & 15;
+  int voff[DBLK];    // V read transposed: rows 8(G>>1) + j/4 (+16kk + 4c), column 32b + 16(G&1) + 4(j%4)
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b) {
+    const int row = 8 * (G >> 1) + (j16 >> 2);
+    const int col = 32 * b + 16 * (G & 1) + 4 * (j16 & 3);
+    voff[b] = row * D + (((col >> 3) ^ v_swz(row)) << 3) + (col & 7);
   }
 
   f32x16 oacc[DBLK];
@@ -90,26 +133,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   for (int b = 0; b < DBLK; ++b)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
-  float m_run = kNegInf;  // running max of s·scale·log2e
-  float l_run = 0.f;      // this lane's part of the running normaliser
+  float m_run = kNegInf;  // reference max of s·scale·log2e (lags the true max by < 2^threshold)
+  float l_run = 0.f;      // this lane's part of the normaliser
 
   const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
   const int ntiles = (kv_end + kBC - 1) / kBC;
-
-  RowTile<D, kThreads> kt;
-  TransTile<D, kThreads> vt;
-  kt.load(Kh, 0, N, tid);
-  vt.load(Vh, 0, N, tid);
+  issue(0, 0);
 
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * kBC;
-    __syncthreads();  // every wave is done reading the previous tile
-    kt.store(sK, tid);
-    vt.store(sVt, tid);
-    __syncthreads();
-    if (t + 1 < ntiles) {  // prefetch the next tile while this one is consumed
-      kt.load(Kh, k0 + kBC, N, tid);
-      vt.load(Vh, k0 + kBC, N, tid);
+    const int st = t & 1;
+    wait_vm_all();
+    __syncthreads();  // tile t is in LDS for every wave; stage st^1 is free again
+    if (t + 1 < ntiles) issue(t + 1, st ^ 1);
+    const bf16* ks = smem + st * 2 * TILE;
+    bf16* vs = smem + st * 2 * TILE + TILE;
+    if (k0 + kBC > N) {  // tail tile: rows past N must read as zero, whatever the loads left
+      const int first = N - k0;
+      for (int idx = tid; idx < (kBC - first) * CPR; idx += kThreads) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(vs + (first + idx / CPR) * D + (idx % CPR) * 8) = z;
+      }
+      __syncthreads();
     }
     if (!wave_live || (CAUSAL && k0 > qw + 31)) continue;
 
@@ -117,11 +162,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(ks + kb * 32 * D + koff[0]), qreg[0], f32x16{});
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const int row = 32 * kb + perm_row(n);
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) s[kb] = mfma32(lds_rm_read<D>(sK, row, 2 * kk + g), qreg[kk], s[kb]);
+      for (int kk = 1; kk < KSTEPS; ++kk)
+        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(ks + kb * 32 * D + koff[kk]), qreg[kk], s[kb]);
     }
 
     // ---- mask: future keys (causal diagonal) and keys past N ----------------
@@ -137,44 +181,52 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         }
     }
 
-    // ---- online softmax ------------------------------------------------------
+    // ---- online softmax with a lazily moved reference max --------------------
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = xhalf_max(mx);
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = exp2_fast(m_run - m_use);
-    float psum = 0.f;
+    mx = xhalf_max(mx) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2_fast(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
     bf16x8 pb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        float p[8];
+        u32x4 w;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = exp2_fast(__builtin_fmaf(s[kb][8 * h + j], scale_log2, -m_use));
-          psum += p[j];
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = exp2_fast(__builtin_fmaf(s[kb][8 * h + 2 * j], scale_log2, -m_use));
+          const float p1 = exp2_fast(__builtin_fmaf(s[kb][8 * h + 2 * j + 1], scale_log2, -m_use));
+          w[j] = pack_bf16x2(p0, p1);
+          l_run += p0 + p1;  // fp32 sum of the unrounded p: the logsumexp needs it exact
         }
-        pb[2 * kb + h] = pack8(p);
+        pb[2 * kb + h] = __builtin_bit_cast(bf16x8, w);
       }
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int b = 0; b < DBLK; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
 
-    // ---- Oᵀ += Vᵀ Pᵀ -----------------------------------------------------------
+    // ---- Oᵀ += Vᵀ Pᵀ (Vᵀ read transposed out of the row-major tile) ----------
 #pragma unroll
     for (int b = 0; b < DBLK; ++b) {
-      const int d = 32 * b + n;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) oacc[b] = mfma32(lds_tr_read(sVt, d, 2 * kk + g), pb[kk], oacc[b]);
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16* base = vs + voff[b] + 16 * kk * D;
+        const bf16x4 lo = lds_read_tr4(base);
+        const bf16x4 hi = lds_read_tr4(base + 4 * D);
+        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[b] = mfma32(a, pb[kk], oacc[b]);
+      }
     }
   }
 
