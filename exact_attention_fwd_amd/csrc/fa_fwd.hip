@@ -51,10 +51,15 @@ __device__ __forceinline__ void map_block(int bid, int nqb, int BH, bool causal,
   bh = head;
 }
 
-// Swizzle of the row-major V tile: the transposed operand reads take four
-// consecutive rows per 16-lane group, so rows r..r+3 get their 32-byte column
-// pieces moved to four different 32-byte bank windows.
-__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 1; }
+// Swizzle of the row-major V tile (16-byte chunk c of row r lives at
+// c ^ v_swz(r)).  A transposed operand read covers four consecutive rows per
+// 16-lane group and 16 columns per group pair; the pattern {0, 10, 4, 14} on
+// r % 4 sends those pieces to distinct banks whether the LDS serves 16 or 32
+// lanes of an 8-byte read per cycle.
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  return ((0xE4A0 >> (4 * (row & 3))) & 15) & (D / 8 - 1);
+}
 
 // Rescale the output only when the running max grows by more than this many
 // powers of two.  Between rescales p = 2^(s·scale·log2e − m) <= 2^8: the
@@ -72,11 +77,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
   constexpr int ROWS_PER_DMA = 64 / CPR;      // rows per 1 KiB wavefront load
   constexpr int DMA_PER_WAVE = kTileRows / ROWS_PER_DMA / kWaves;
-  // [stage][K, V][64][D], both row-major; two stages form a load/compute ring
-  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * 2 * TILE];
+  // K ring (2 tiles) then V ring (2 tiles), all row-major [64][D].  K runs one
+  // tile ahead of V: while tile t is consumed, K(t+1) is already resident.
+  __shared__ __attribute__((aligned(1024))) bf16 smem[4 * TILE];
+  bf16* const kring = smem;
+  bf16* const vring = smem + 2 * TILE;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
   const int nqb = (N + kBR - 1) / kBR;
   int qb, bh;
@@ -90,7 +99,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int q0 = qb * kBR;
   const int qw = q0 + wave * 32;
   const int qrow = qw + n;  // this lane's query
-  const bool wave_live = qw < N;
 
   // Qᵀ as the B operand: lane (g, n) holds Q[qrow][16kk + 8g .. +7] (zeros past N).
   bf16x8 qreg[KSTEPS];
@@ -98,21 +106,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   for (int kk = 0; kk < KSTEPS; ++kk)
     qreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)qrow * (D * 2) + (16 * kk + 8 * g) * 2));
 
-  // Direct-to-LDS loads of tile t into stage st: wave w fills 1 KiB blocks
-  // w*DMA_PER_WAVE .. of both tiles; lane l writes physical chunk l % CPR of
-  // row l / CPR of its block, fetching the logical chunk that swizzles there.
+  // Direct-to-LDS loads: wave w fills 1 KiB blocks w*DMA_PER_WAVE.. of a tile;
+  // lane l writes physical chunk l % CPR of row l / CPR of its block, fetching
+  // the logical chunk that the tile's swizzle puts there.
   const int dma_row = lane / CPR, dma_pc = lane % CPR;
-  auto issue = [&](int t, int st) {
-    bf16* ks = smem + st * 2 * TILE;
-    bf16* vs = ks + TILE;
+  uint32_t kdma[DMA_PER_WAVE], vdma[DMA_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      const int blk = wave * DMA_PER_WAVE + i;
-      const int row = blk * ROWS_PER_DMA + dma_row;
-      const uint32_t roff = (uint32_t)(t * kTileRows + row) * (D * 2);
-      lds_dma16(rk, ks + blk * 512, roff + ((dma_pc ^ rm_swz<D>(row)) << 4));
-      lds_dma16(rv, vs + blk * 512, roff + ((dma_pc ^ v_swz(row)) << 4));
-    }
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int row = (wave * DMA_PER_WAVE + i) * ROWS_PER_DMA + dma_row;
+    kdma[i] = (uint32_t)row * (D * 2) + ((dma_pc ^ rm_swz<D>(row)) << 4);
+    vdma[i] = (uint32_t)row * (D * 2) + ((dma_pc ^ v_swz<D>(row)) << 4);
+  }
+  auto issue_k = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i)
+      lds_dma16(rk, kring + (t & 1) * TILE + (wave * DMA_PER_WAVE + i) * 512, kdma[i] + (uint32_t)t * (64 * D * 2));
+  };
+  auto issue_v = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i)
+      lds_dma16(rv, vring + (t & 1) * TILE + (wave * DMA_PER_WAVE + i) * 512, vdma[i] + (uint32_t)t * (64 * D * 2));
   };
 
   // Per-lane LDS element offsets of the operand reads (loop invariant).
@@ -125,8 +138,40 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   for (int b = 0; b < DBLK; ++b) {
     const int row = 8 * (G >> 1) + (j16 >> 2);
     const int col = 32 * b + 16 * (G & 1) + 4 * (j16 & 3);
-    voff[b] = row * D + (((col >> 3) ^ v_swz(row)) << 3) + (col & 7);
+    voff[b] = row * D + (((col >> 3) ^ v_swz<D>(row)) << 3) + (col & 7);
   }
+
+  // Sᵀ = K Qᵀ for one 64-key tile (16 LDS reads + 16 MFMA).
+  auto scores = [&](const bf16* ks, f32x16* s) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(ks + kb * 32 * D + koff[0]), qreg[0], f32x16{});
+#pragma unroll
+      for (int kk = 1; kk < KSTEPS; ++kk)
+        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(ks + kb * 32 * D + koff[kk]), qreg[kk], s[kb]);
+    }
+  };
+  // Future keys (causal diagonal) and keys past N get -inf.
+  auto mask = [&](int k0, f32x16* s) {
+    if ((CAUSAL && k0 + kBC - 1 > qw) || (k0 + kBC > N)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + crow(kb, r, g);
+          const bool dead = (key >= N) || (CAUSAL && key > qrow);
+          s[kb][r] = dead ? kNegInf : s[kb][r];
+        }
+    }
+  };
+  auto tile_max = [&](const f32x16* s) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    return xhalf_max(mx) * scale_log2;
+  };
 
   f32x16 oacc[DBLK];
 #pragma unroll
@@ -138,17 +183,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
   const int ntiles = (kv_end + kBC - 1) / kBC;
-  issue(0, 0);
+  // tiles this wave needs (causal: up to its last query; none past N)
+  const int wnt = (qw >= N) ? 0 : (CAUSAL ? min(ntiles, (min(qw + 31, N - 1) / kBC) + 1) : ntiles);
 
-  for (int t = 0; t < ntiles; ++t) {
+  issue_k(0);
+  if (ntiles > 1) issue_k(1);
+  issue_v(0);
+  wait_vm_all();
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  if (wnt > 0) {
+    scores(kring, sa);
+    mask(0, sa);
+    m_run = tile_max(sa);  // first tile: nothing to rescale yet
+  }
+
+  // One tile: P(t) from S(t) = sc, while S(t+1) = sn is computed on the matrix
+  // pipe; then O += V(t)ᵀ P(t); then S(t+1) is masked and its max checked.
+  auto step = [&](int t, f32x16* sc, f32x16* sn) {
     const int k0 = t * kBC;
-    const int st = t & 1;
     wait_vm_all();
-    __syncthreads();  // tile t is in LDS for every wave; stage st^1 is free again
-    if (t + 1 < ntiles) issue(t + 1, st ^ 1);
-    const bf16* ks = smem + st * 2 * TILE;
-    bf16* vs = smem + st * 2 * TILE + TILE;
-    if (k0 + kBC > N) {  // tail tile: rows past N must read as zero, whatever the loads left
+    __syncthreads();  // K(t+1) and V(t) resident for every wave; tile t-1 fully consumed
+    if (t + 2 < ntiles) issue_k(t + 2);
+    if (t + 1 < ntiles) issue_v(t + 1);
+    bf16* vs = vring + (t & 1) * TILE;
+    if (k0 + kBC > N) {  // tail tile: V rows past N must read as zero, whatever the loads left
       const int first = N - k0;
       for (int idx = tid; idx < (kBC - first) * CPR; idx += kThreads) {
         const u32x4 z = {0u, 0u, 0u, 0u};
@@ -156,48 +215,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       }
       __syncthreads();
     }
-    if (!wave_live || (CAUSAL && k0 > qw + 31)) continue;
+    if (t >= wnt) return;
 
-    // ---- Sᵀ = K Qᵀ : two 32-key blocks -------------------------------------
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(ks + kb * 32 * D + koff[0]), qreg[0], f32x16{});
-#pragma unroll
-      for (int kk = 1; kk < KSTEPS; ++kk)
-        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(ks + kb * 32 * D + koff[kk]), qreg[kk], s[kb]);
-    }
+    // On a wave's last tile this product reads a stale K tile and is dropped.
+    scores(kring + ((t + 1) & 1) * TILE, sn);
 
-    // ---- mask: future keys (causal diagonal) and keys past N ----------------
-    const bool need_mask = (CAUSAL && k0 + kBC - 1 > qw) || (k0 + kBC > N);
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + crow(kb, r, g);
-          const bool dead = (key >= N) || (CAUSAL && key > qrow);
-          s[kb][r] = dead ? kNegInf : s[kb][r];
-        }
-    }
-
-    // ---- online softmax with a lazily moved reference max --------------------
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = xhalf_max(mx) * scale_log2;
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2_fast(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int b = 0; b < DBLK; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
-      m_run = m_new;
-    }
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
     bf16x8 pb[4];
 #pragma unroll
@@ -207,8 +229,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         u32x4 w;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p0 = exp2_fast(__builtin_fmaf(s[kb][8 * h + 2 * j], scale_log2, -m_use));
-          const float p1 = exp2_fast(__builtin_fmaf(s[kb][8 * h + 2 * j + 1], scale_log2, -m_use));
+          const float p0 = exp2_fast(__builtin_fmaf(sc[kb][8 * h + 2 * j], scale_log2, -m_use));
+          const float p1 = exp2_fast(__builtin_fmaf(sc[kb][8 * h + 2 * j + 1], scale_log2, -m_use));
           w[j] = pack_bf16x2(p0, p1);
           l_run += p0 + p1;  // fp32 sum of the unrounded p: the logsumexp needs it exact
         }
@@ -216,7 +238,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       }
     }
 
-    // ---- Oᵀ += Vᵀ Pᵀ (Vᵀ read transposed out of the row-major tile) ----------
+    // Oᵀ += Vᵀ Pᵀ (Vᵀ read transposed out of the row-major tile)
 #pragma unroll
     for (int b = 0; b < DBLK; ++b) {
 #pragma unroll
@@ -228,9 +250,44 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         oacc[b] = mfma32(a, pb[kk], oacc[b]);
       }
     }
+    // Interleave: each S(t+1) product with a K read and a slice of the
+    // softmax VALU work, then the P·V products with their transposed reads.
+#pragma unroll
+    for (int i = 0; i < 2 * KSTEPS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // VALU
+    }
+#pragma unroll
+    for (int i = 0; i < 4 * DBLK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS transposed reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU
+    }
+
+    // Move the reference max for tile t+1 if it grew too far (O now holds tile t).
+    if (t + 1 < wnt) {
+      mask(k0 + kBC, sn);
+      const float mx = tile_max(sn);
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = exp2_fast(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+        m_run = m_new;
+      }
+    }
+  };
+
+  for (int t = 0; t < ntiles; t += 2) {  // unrolled by two so S(t) and S(t+1) swap registers
+    step(t, sa, sb);
+    if (t + 1 < ntiles) step(t + 1, sb, sa);
   }
 
-  if (!wave_live || qrow >= N) return;
+  if (qw >= N || qrow >= N) return;
   const float l_tot = xhalf_sum(l_run);
   const float inv = 1.f / l_tot;
   bf16* Orow = O + head_off + (size_t)qrow * D;
