@@ -51,7 +51,8 @@ size_t backward_workspace_bytes(long long BH, long long N) {
 
 size_t decode_workspace_bytes(long long S, long long H, long long d, long long max_blocks) {
   if (S <= 0 || H <= 0 || d <= 0 || max_blocks <= 0) return 0;
-  return round256((size_t)S * H * max_blocks * (size_t)(d + 2) * sizeof(float));
+  // two 128-token splits per 256-token page
+  return round256((size_t)S * H * max_blocks * 2 * (size_t)(d + 2) * sizeof(float));
 }
 
 }  // namespace fa
@@ -131,7 +132,7 @@ fa_status fa_decode_paged(int num_seqs, int H, int d, int page_size, int num_pag
   if (page_size != 256) return FA_ERR_UNSUPPORTED;
   if (H > 4096 || !fits(num_pages, 2, page_size, (long long)H * d) ||
       !fits(num_seqs, H, max_blocks_per_seq, d + 2) || (long long)max_blocks_per_seq * page_size > INT_MAX ||
-      (long long)num_seqs * max_blocks_per_seq * H > INT_MAX)  // grid of the split kernel
+      (long long)num_seqs * max_blocks_per_seq * 2 * H > INT_MAX)  // grid of the split kernel
     return FA_ERR_BAD_SHAPE;
   if (!std::isfinite(scale)) return FA_ERR_BAD_SHAPE;
   if (!q || !kv_pool || !block_table || !seq_lens || !o) return FA_ERR_NULL_PTR;

@@ -8,9 +8,12 @@
 // head's 256-byte K row of one token is read by 16 lanes (16 bytes each), so
 // the 8 heads of one token are a contiguous 2 KiB read by two wavefronts.
 // Each lane keeps the online-softmax state of its (token parity, head, 8
-// features) over blocks of 8 tokens; scores are reduced over the 16 lanes
-// with DPP.  The result per (sequence, head, page) is the partial running
-// max, normaliser and unnormalised output.
+// features) over blocks of 8 tokens.  Scores are bf16 dot products
+// (v_dot2_f32_bf16, fp32 accumulate) reduced over the 16 lanes with DPP;
+// p·V runs as dot2 over token pairs.  K/V are read through buffer
+// descriptors that end at the sequence's last token, so slots past it are
+// never fetched.  The result per (sequence, head, page) is the partial
+// running max, normaliser and unnormalised output.
 // Kernel 2 (merge): combines the partials of a (sequence, head) exactly:
 // m = max m_b, l = Σ 2^(m_b − m) l_b, O = Σ 2^(m_b − m) õ_b / l — the running
 // max / normaliser update of "Flash Attention 是什么" (ai.lansai.wang),
@@ -24,7 +27,9 @@ namespace {
 
 constexpr int kDecThreads = 256;
 constexpr int kPage = 256;
-constexpr int kUnroll = 8;
+constexpr int kSplit = 128;                 // tokens per workgroup (two splits per page)
+constexpr int kSplitsPerPage = kPage / kSplit;
+constexpr int kUnroll = 8;                  // tokens per lane per load batch
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -41,12 +46,12 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ void bf16x8_to_f32(const u32x4& w, float* f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(w[i] << 16);
-    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
+// Rescale the partial output only when the running max grows by more than
+// 2^8 (same reference max for output, normaliser and logsumexp: exact).
+constexpr float kRescaleThreshold = 8.0f;
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
 template <int D, int HG>
@@ -55,18 +60,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const int32_t* __restrict__ seq_lens, float* __restrict__ part, int H, int max_blocks, float scale_log2) {
   constexpr int LPR = D / 8;                       // lanes per (token, head) row
   constexpr int TP = kDecThreads / (HG * LPR);     // tokens handled side by side
-  constexpr int STEPS = kPage / TP;                // tokens per lane in one page
-  static_assert(STEPS % kUnroll == 0, "page must split evenly");
+  constexpr int STEPS = kSplit / TP;               // tokens per lane in one split
+  constexpr int U = (STEPS / 2 < kUnroll) ? STEPS / 2 : kUnroll;  // tokens per lane per batch
+  static_assert(STEPS % (2 * U) == 0 && U % 2 == 0, "split must divide into pairs of batches");
   __shared__ float red[TP][HG][D + 2];
 
   const int hgroups = H / HG;
-  const int s = blockIdx.x / (max_blocks * hgroups);
-  const int rem = blockIdx.x % (max_blocks * hgroups);
-  const int b = rem / hgroups;
+  const int nsplit = max_blocks * kSplitsPerPage;
+  const int s = blockIdx.x / (nsplit * hgroups);
+  const int rem = blockIdx.x % (nsplit * hgroups);
+  const int sp = rem / hgroups;                    // split index within the sequence
   const int h0 = (rem % hgroups) * HG;
+  const int b = sp / kSplitsPerPage;               // logical page
+  const int t0 = (sp % kSplitsPerPage) * kSplit;   // first slot of this split in the page
   const int L = seq_lens[s];
-  const int ntok = min(kPage, L - b * kPage);
-  if (ntok <= 0) return;  // this page is past the sequence end
+  const int ntok = min(kSplit, L - b * kPage - t0);
+  if (ntok <= 0) return;  // this split is past the sequence end
   const int page = block_table[(size_t)s * max_blocks + b];
 
   const int tid = threadIdx.x;
@@ -75,59 +84,77 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const int tp = tid / (LPR * HG);
   const int h = h0 + hh;
 
-  float qf[8];
-  bf16x8_to_f32(*reinterpret_cast<const u32x4*>(q + ((size_t)s * H + h) * D + c * 8), qf);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) qf[e] *= scale_log2;
+  // This lane's 8 query features, packed bf16 pairs (exact input values).
+  const u32x4 qv = *reinterpret_cast<const u32x4*>(q + ((size_t)s * H + h) * D + c * 8);
 
-  const size_t tok_stride = (size_t)H * D;
-  const bf16* Kp = pool + (size_t)page * 2 * kPage * tok_stride + (size_t)h * D + c * 8;
-  const bf16* Vp = Kp + (size_t)kPage * tok_stride;
+  // K and V of this split as bounds-checked buffers covering exactly its
+  // valid tokens: a slot at or past L reads as zero and is never fetched.
+  const uint32_t tok_bytes = (uint32_t)H * D * 2;
+  const bf16* kbase = pool + (size_t)page * 2 * kPage * H * D + (size_t)t0 * H * D;
+  const auto rk = make_rsrc(kbase, (uint32_t)ntok * tok_bytes);
+  const auto rv = make_rsrc(kbase + (size_t)kPage * H * D, (uint32_t)ntok * tok_bytes);
+  const uint32_t lane_off = (uint32_t)(h * D + c * 8) * 2;
 
   float m = kNegInf, l = 0.f, o[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
 
-  for (int i0 = 0; i0 < STEPS; i0 += kUnroll) {
-    u32x4 kr[kUnroll], vr[kUnroll];
+  auto load = [&](int i0, u32x4* kr, u32x4* vr) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int t = tp + TP * (i0 + u);
-      const bool ok = t < ntok;
-      u32x4 zero = {0u, 0u, 0u, 0u};
-      kr[u] = ok ? *reinterpret_cast<const u32x4*>(Kp + t * tok_stride) : zero;
-      vr[u] = ok ? *reinterpret_cast<const u32x4*>(Vp + t * tok_stride) : zero;
+    for (int u = 0; u < U; ++u) {
+      const uint32_t off = (uint32_t)(tp + TP * (i0 + u)) * tok_bytes + lane_off;
+      kr[u] = buf_load16_stream(rk, off);
+      vr[u] = buf_load16_stream(rv, off);
     }
-    float sc[kUnroll];
+  };
+  auto consume = [&](int i0, const u32x4* kr, const u32x4* vr) {
+    float sc[U];
     float bmax = kNegInf;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      float kf[8];
-      bf16x8_to_f32(kr[u], kf);
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qf[e], kf[e], acc);
-      acc = group_sum<LPR>(acc);
-      const int t = tp + TP * (i0 + u);
-      sc[u] = (t < ntok) ? acc : kNegInf;
+    for (int u = 0; u < U; ++u) {
+      float acc = dot2(qv[0], kr[u][0], 0.f);
+      acc = dot2(qv[1], kr[u][1], acc);
+      acc = dot2(qv[2], kr[u][2], acc);
+      acc = dot2(qv[3], kr[u][3], acc);
+      acc = group_sum<LPR>(acc) * scale_log2;
+      sc[u] = (tp + TP * (i0 + u) < ntok) ? acc : kNegInf;
       bmax = fmaxf(bmax, sc[u]);
     }
-    if (bmax == kNegInf) continue;  // every token of this block is past the end
-    const float m_new = fmaxf(m, bmax);
-    const float alpha = exp2_fast(m - m_new);
-    l *= alpha;
+    if (bmax > m + kRescaleThreshold) {  // uniform over the 16-lane row group
+      const float alpha = exp2_fast(m - bmax);
+      l *= alpha;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] *= alpha;
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const float p = exp2_fast(sc[u] - m_new);  // 0 for tokens past the end
-      l += p;
-      float vf[8];
-      bf16x8_to_f32(vr[u], vf);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(p, vf[e], o[e]);
+      for (int e = 0; e < 8; ++e) o[e] *= alpha;
+      m = bmax;
     }
-    m = m_new;
+    // o += p·v over token pairs: p packed to bf16, v regrouped into
+    // (token u, token u+1) pairs per feature, one dot2 per feature pair.
+    // A stream that has seen no valid token yet keeps m = -inf; its p are 0.
+    const float m_use = (m == kNegInf) ? 0.f : m;
+#pragma unroll
+    for (int u = 0; u < U; u += 2) {
+      const float p0 = exp2_fast(sc[u] - m_use), p1 = exp2_fast(sc[u + 1] - m_use);
+      l += p0 + p1;
+      const uint32_t pp = pack_bf16x2(p0, p1);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = __builtin_amdgcn_perm(vr[u + 1][w], vr[u][w], 0x05040100u);  // (v_u[2w],   v_u+1[2w])
+        const uint32_t hi = __builtin_amdgcn_perm(vr[u + 1][w], vr[u][w], 0x07060302u);  // (v_u[2w+1], v_u+1[2w+1])
+        o[2 * w] = dot2(pp, lo, o[2 * w]);
+        o[2 * w + 1] = dot2(pp, hi, o[2 * w + 1]);
+      }
+    }
+  };
+
+  // Two register batches: the next batch's loads are in flight while the
+  // current one is consumed.
+  u32x4 ka[U], va[U], kb2[U], vb2[U];
+  load(0, ka, va);
+  for (int i0 = 0; i0 < STEPS; i0 += 2 * U) {
+    load(i0 + U, kb2, vb2);
+    consume(i0, ka, va);
+    if (i0 + 2 * U < STEPS) load(i0 + 2 * U, ka, va);
+    consume(i0 + U, kb2, vb2);
   }
 
   // Merge the TP token streams of each (head, feature chunk) through LDS.
@@ -154,7 +181,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) oo[e] += w * red[j][hh][c * 8 + e];
   }
-  float* out = part + (((size_t)s * H + h) * max_blocks + b) * (D + 2);
+  float* out = part + (((size_t)s * H + h) * nsplit + sp) * (D + 2);
 #pragma unroll
   for (int e = 0; e < 8; ++e) out[c * 8 + e] = oo[e];
   if (c == 0) {
@@ -163,41 +190,64 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   }
 }
 
-// One wavefront per (sequence, head): merge the per-page partial states.
+// One wavefront per (sequence, head): merge the per-split partial states.
+// Lane j holds split j's (m, l); the output features are split over lanes
+// and the splits' rows are loaded in independent batches of eight.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ part,
                                                           const int32_t* __restrict__ seq_lens,
                                                           bf16* __restrict__ O, float* __restrict__ LSE, int H,
                                                           int max_blocks) {
   constexpr int PER = D / 64;
+  constexpr int BATCH = 8;
   const int sh = blockIdx.x;
   const int s = sh / H;
   const int lane = threadIdx.x;
-  const int nb = (seq_lens[s] + kPage - 1) / kPage;
-  const float* p = part + (size_t)sh * max_blocks * (D + 2);
-  float m = kNegInf;
-  for (int b = 0; b < nb; ++b) m = fmaxf(m, p[(size_t)b * (D + 2) + D]);
-  float l = 0.f, o[PER];
+  const int nsplit = max_blocks * kSplitsPerPage;
+  const int ns = (seq_lens[s] + kSplit - 1) / kSplit;
+  const float* p = part + (size_t)sh * nsplit * (D + 2);
+  float m = kNegInf, o[PER], lsum = 0.f;
 #pragma unroll
   for (int e = 0; e < PER; ++e) o[e] = 0.f;
-  for (int b = 0; b < nb; ++b) {
-    const float* pb = p + (size_t)b * (D + 2);
-    const float w = exp2_fast(pb[D] - m);
-    l += w * pb[D + 1];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] += w * pb[lane * PER + e];
+  for (int j0 = 0; j0 < ns; j0 += 64) {
+    const int j = j0 + lane;
+    m = fmaxf(m, j < ns ? p[(size_t)j * (D + 2) + D] : kNegInf);
   }
-  const float inv = 1.f / l;
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  for (int j0 = 0; j0 < ns; j0 += 64) {
+    const int j = j0 + lane;
+    const float w = j < ns ? exp2_fast(p[(size_t)j * (D + 2) + D] - m) : 0.f;
+    lsum += j < ns ? w * p[(size_t)j * (D + 2) + D + 1] : 0.f;
+    const int cnt = min(64, ns - j0);
+    for (int i0 = 0; i0 < cnt; i0 += BATCH) {
+      float v[BATCH][PER];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const float* pj = p + (size_t)(j0 + min(i0 + i, cnt - 1)) * (D + 2) + lane * PER;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[i][e] = pj[e];
+      }
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), (i0 + i) & 63));
+        const float wk = (i0 + i < cnt) ? wi : 0.f;  // split j0+i0+i's weight
+#pragma unroll
+        for (int e = 0; e < PER; ++e) o[e] += wk * v[i][e];
+      }
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
+  const float inv = 1.f / lsum;
   bf16* orow = O + (size_t)sh * D;
 #pragma unroll
   for (int e = 0; e < PER; ++e) orow[lane * PER + e] = (bf16)(o[e] * inv);
-  if (LSE != nullptr && lane == 0) LSE[sh] = (m + log2_fast(l)) * kLn2;
+  if (LSE != nullptr && lane == 0) LSE[sh] = (m + log2_fast(lsum)) * kLn2;
 }
 
 template <int D, int HG>
 hipError_t launch(const DecodeArgs& a) {
   const int hgroups = a.H / HG;
-  const dim3 grid1((unsigned)(a.S * a.max_blocks * hgroups)), block1(kDecThreads);
+  const dim3 grid1((unsigned)(a.S * a.max_blocks * kSplitsPerPage * hgroups)), block1(kDecThreads);
   hipLaunchKernelGGL((decode_split_kernel<D, HG>), grid1, block1, 0, a.stream, static_cast<const bf16*>(a.q),
                      static_cast<const bf16*>(a.kv_pool), a.block_table, a.seq_lens, a.part, a.H, a.max_blocks,
                      a.scale * kLog2e);

@@ -120,8 +120,9 @@ fa_status fa_backward(fa_dtype dt, int B, int H, int N, int d,
 
 /*
  * Workspace for fa_decode_paged in bytes: per (sequence, head, KV split) a
- * partial running max, normaliser and unnormalised output row in fp32, with
- * at most max_blocks_per_seq splits per sequence.
+ * partial running max, normaliser and unnormalised output row in fp32; a
+ * split is half a 256-token page, so at most 2·max_blocks_per_seq splits
+ * per sequence.
  */
 size_t fa_decode_workspace_bytes(int num_seqs, int H, int d, int max_blocks_per_seq);
 
