@@ -16,6 +16,11 @@
 //   bwd_dq    : a workgroup owns 128 queries and walks their key tiles, with
 //               Sᵀ held as [key rows x query column per lane] as in the
 //               forward.
+// Q/dO (dK/dV pass) and K/V (dQ pass) tiles go HBM -> LDS with direct
+// buffer loads into a two-stage ring; the transposed operands (dOᵀ, Qᵀ, Kᵀ)
+// are read out of the same row-major tiles with ds_read_b64_tr_b16.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -55,8 +60,78 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const bf16* __restr
   if (row < rows && c == 0) delta[row] = acc;
 }
 
+// Direct-to-LDS loads of a 64-row tile of a [rows, D] matrix (row-major in
+// LDS, dual-swizzled): wave w fills 1 KiB blocks w*DPW.. of the tile.
+template <int D>
+struct TileDma {
+  static constexpr int CPR = D / 8;
+  static constexpr int RPD = 64 / CPR;               // rows per 1 KiB block
+  static constexpr int DPW = kTileRows / RPD / 4;    // blocks per wave
+  uint32_t off[DPW];
+  int base_blk;
+  __device__ __forceinline__ void init(int wave, int lane) {
+    base_blk = wave * DPW;
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+      const int row = (base_blk + i) * RPD + lane / CPR;
+      off[i] = (uint32_t)row * (D * 2) + (((lane % CPR) ^ dual_swz<D>(row)) << 4);
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, bf16* tile, int row0) const {
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) lds_dma16(r, tile + (base_blk + i) * 512, off[i] + (uint32_t)row0 * (D * 2));
+  }
+};
+
+// Per-lane element offsets of the two operand reads of a dual-swizzled tile.
+template <int D>
+struct TileReads {
+  static constexpr int KSTEPS = D / 16, DBLK = D / 32;
+  int rm[KSTEPS];     // row-major A operand: row perm_row(n) (+32 kb), chunk 2kk+g
+  int tr[DBLK][2];    // transposed A operand: rows 8(G>>1) + 4c + j/4 (+16 kk), column 32b + 16(G&1) + 4(j%4)
+  __device__ __forceinline__ void init(int lane) {
+    const int g = lane >> 5, n = lane & 31;
+    const int pr = perm_row(n);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) rm[kk] = pr * D + (((2 * kk + g) ^ dual_swz<D>(pr)) << 3);
+    const int G = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int row = 8 * (G >> 1) + 4 * c + (j >> 2);
+        const int col = 32 * b + 16 * (G & 1) + 4 * (j & 3);
+        tr[b][c] = row * D + (((col >> 3) ^ dual_swz<D>(row)) << 3) + (col & 7);
+      }
+  }
+  // rows 32kb.. of the tile, k-step kk over the head dim
+  __device__ __forceinline__ bf16x8 row_major(const bf16* tile, int kb, int kk) const {
+    return *reinterpret_cast<const bf16x8*>(tile + kb * 32 * D + rm[kk]);
+  }
+  // head-dim rows 32b.., k-step kk over the tile's rows (16kk .. 16kk+15)
+  __device__ __forceinline__ bf16x8 transposed(const bf16* tile, int b, int kk) const {
+    const bf16x4 lo = lds_read_tr4(tile + tr[b][0] + 16 * kk * D);
+    const bf16x4 hi = lds_read_tr4(tile + tr[b][1] + 16 * kk * D);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+
+// Zero rows [first, 64) of a row-major tile (all chunks), block-wide.
+template <int D>
+__device__ __forceinline__ void zero_rows(bf16* tile, int first, int tid) {
+  constexpr int CPR = D / 8;
+  for (int idx = tid; idx < (kTileRows - first) * CPR; idx += kThreads) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(tile + (first + idx / CPR) * D + (idx % CPR) * 8) = z;
+  }
+}
+
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup = 128 keys of one head; wavefront w owns keys kw..kw+31.
+// dK, dV: workgroup = 128 keys of one head; wavefront w owns keys kw..kw+31
+// and walks the 64-query tiles that see them (Q and dO tiles in an LDS ring).
+// S = Q Kᵀ and dP = dO Vᵀ are held as [32 query rows x this lane's key], so
+// P and dS feed dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS directly as B operands, with
+// dOᵀ and Qᵀ read transposed out of the same tiles.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
@@ -65,39 +140,34 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     bf16* __restrict__ dK, bf16* __restrict__ dV, int N, float scale, float scale_log2) {
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
-  constexpr int BQ = kTileRows;  // queries per step
-  __shared__ __attribute__((aligned(16))) bf16 sQ[BQ * D];
-  __shared__ __attribute__((aligned(16))) bf16 sQt[D * BQ];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[BQ * D];
-  __shared__ __attribute__((aligned(16))) bf16 sdOt[D * BQ];
-  __shared__ __attribute__((aligned(16))) float sL[BQ];
-  __shared__ __attribute__((aligned(16))) float sDl[BQ];
+  constexpr int TILE = kTileRows * D;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * 2 * TILE];  // [stage][Q, dO]
+  __shared__ __attribute__((aligned(16))) float sstat[2][2][kTileRows];  // [stage][LSE·log2e, D]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
   const int bh = blockIdx.y;
   const int k0 = blockIdx.x * 128;
   const int kw = k0 + 32 * wave;
   const int key = kw + n;  // this lane's key column
-  const bool wave_live = kw < N;
   const size_t head_off = (size_t)bh * N * D;
-  const bf16* Qh = Q + head_off;
-  const bf16* dOh = dO + head_off;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto rq = make_rsrc(Q + head_off, head_bytes);
+  const auto rdo = make_rsrc(dO + head_off, head_bytes);
+  const auto rk = make_rsrc(K + head_off, head_bytes);
+  const auto rv = make_rsrc(V + head_off, head_bytes);
   const float* Lh = LSE + (size_t)bh * N;
   const float* Dh = delta + (size_t)bh * N;
 
-  // Kᵀ and Vᵀ as B operands: lane (g, n) holds row `key`, features 16kk+8g..
+  // Kᵀ and Vᵀ as B operands: lane (g, n) holds row `key`, features 16kk+8g.. (zeros past N).
   bf16x8 kreg[KSTEPS], vreg[KSTEPS];
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
-    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (key < N) {
-      x = *reinterpret_cast<const u32x4*>(K + head_off + (size_t)key * D + 16 * kk + 8 * g);
-      y = *reinterpret_cast<const u32x4*>(V + head_off + (size_t)key * D + 16 * kk + 8 * g);
-    }
-    kreg[kk] = __builtin_bit_cast(bf16x8, x);
-    vreg[kk] = __builtin_bit_cast(bf16x8, y);
+    const uint32_t off = (uint32_t)key * (D * 2) + (16 * kk + 8 * g) * 2;
+    kreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
+    vreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
   }
   f32x16 dk[DBLK], dv[DBLK];
 #pragma unroll
@@ -108,73 +178,112 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       dv[b][r] = 0.f;
     }
 
-  const int qstart = CAUSAL ? (k0 / BQ) * BQ : 0;
-  for (int q0 = qstart; q0 < N; q0 += BQ) {
-    __syncthreads();
-    {
-      RowTile<D, kThreads> t;
-      t.load(Qh, q0, N, tid);
-      t.store(sQ, tid);
-      t.load(dOh, q0, N, tid);
-      t.store(sdO, tid);
-      TransTile<D, kThreads> u;
-      u.load(Qh, q0, N, tid);
-      u.store(sQt, tid);
-      u.load(dOh, q0, N, tid);
-      u.store(sdOt, tid);
-      if (tid < BQ) {
-        const bool ok = q0 + tid < N;
-        sL[tid] = ok ? Lh[q0 + tid] * kLog2e : 0.f;
-        sDl[tid] = ok ? Dh[q0 + tid] : 0.f;
-      }
-    }
-    __syncthreads();
-    if (!wave_live || (CAUSAL && q0 + BQ - 1 < kw)) continue;
-    const bool need_mask = (CAUSAL && q0 < kw + 31) || (q0 + BQ > N) || (kw + 32 > N);
+  TileDma<D> dma;
+  dma.init(wave, lane);
+  TileReads<D> rd;
+  rd.init(lane);
 
+  const int qstart = CAUSAL ? k0 : 0;  // k0 is a multiple of the 64-query tile
+  const int ntiles = (N - qstart + kTileRows - 1) / kTileRows;
+  auto issue = [&](int i) {
+    bf16* st = smem + (i & 1) * 2 * TILE;
+    dma.issue(rq, st, qstart + i * kTileRows);
+    dma.issue(rdo, st + TILE, qstart + i * kTileRows);
+  };
+  auto load_stat = [&](int i) {  // tid < 64: LSE·log2e, 64 <= tid < 128: D
+    const int q = qstart + i * kTileRows + (tid & 63);
+    float x = 0.f;
+    if (tid < 128 && q < N) x = (tid < 64) ? Lh[q] * kLog2e : Dh[q];
+    return x;
+  };
+  float stat_next = 0.f;
+  issue(0);
+  stat_next = load_stat(0);
+
+  for (int i = 0; i < ntiles; ++i) {
+    const int q0 = qstart + i * kTileRows;
+    const int st = i & 1;
+    if (tid < 128) sstat[st][tid >> 6][tid & 63] = stat_next;
+    wait_vm_all();
+    __syncthreads();  // tile i resident; tile i-1 consumed by every wave
+    if (i + 1 < ntiles) {
+      issue(i + 1);
+      stat_next = load_stat(i + 1);
+    }
+    bf16* qt = smem + st * 2 * TILE;
+    bf16* dot = qt + TILE;
+    if (q0 + kTileRows > N) {  // tail: rows past N must be zero for the transposed products
+      zero_rows<D>(qt, N - q0, tid);
+      zero_rows<D>(dot, N - q0, tid);
+      __syncthreads();
+    }
+    if (kw >= N || (CAUSAL && q0 + kTileRows - 1 < kw)) continue;  // no query of the tile sees these keys
+    const float* lse2 = sstat[st][0];
+    const float* dlt = sstat[st][1];
+
+    // S = Q Kᵀ and dP = dO Vᵀ for the 32 queries of block qb.
+    auto sdp = [&](int qb, f32x16& sv, f32x16& dpv) {
+      sv = mfma32(rd.row_major(qt, qb, 0), kreg[0], f32x16{});
+      dpv = mfma32(rd.row_major(dot, qb, 0), vreg[0], f32x16{});
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      // S = Q Kᵀ and dP = dO Vᵀ for 32 queries (rows) x this lane's key.
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
+      for (int kk = 1; kk < KSTEPS; ++kk) {
+        sv = mfma32(rd.row_major(qt, qb, kk), kreg[kk], sv);
+        dpv = mfma32(rd.row_major(dot, qb, kk), vreg[kk], dpv);
       }
-      const int row = 32 * qb + perm_row(n);
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        s = mfma32(lds_rm_read<D>(sQ, row, 2 * kk + g), kreg[kk], s);
-        dp = mfma32(lds_rm_read<D>(sdO, row, 2 * kk + g), vreg[kk], dp);
-      }
+    };
+    // P = exp(S·scale − LSE) and dS = P ∘ (dP − D), rounded to bf16 pairs of k-steps.
+    auto grads = [&](auto masked, int qb, const f32x16& sv, const f32x16& dpv, bf16x8* pk, bf16x8* dsk) {
       float p[16], ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = crow(qb, r, g);
-        float pr = exp2_fast(__builtin_fmaf(s[r], scale_log2, -sL[qi]));
-        if (need_mask) {
+        float pr = exp2_fast(__builtin_fmaf(sv[r], scale_log2, -lse2[qi]));
+        float dsr = pr * (dpv[r] - dlt[qi]);
+        if constexpr (decltype(masked)::value) {
           const int qa = q0 + qi;
           const bool dead = qa >= N || key >= N || (CAUSAL && key > qa);
           pr = dead ? 0.f : pr;
+          dsr = dead ? 0.f : dsr;
         }
         p[r] = pr;
-        ds[r] = pr * (dp[r] - sDl[qi]);
+        ds[r] = dsr;
       }
-      const bf16x8 p0 = pack8(p), p1 = pack8(p + 8);
-      const bf16x8 d0 = pack8(ds), d1 = pack8(ds + 8);
-      // dVᵀ += dOᵀ P ; dKᵀ += Qᵀ dS   (k-steps over this block's 32 queries)
+      pk[0] = pack8(p);
+      pk[1] = pack8(p + 8);
+      dsk[0] = pack8(ds);
+      dsk[1] = pack8(ds + 8);
+    };
+    // dVᵀ += dOᵀ P ; dKᵀ += Qᵀ dS  (k-steps 2qb, 2qb+1 over the tile's queries)
+    auto accumulate = [&](int qb, const bf16x8* pk, const bf16x8* dsk) {
 #pragma unroll
       for (int b = 0; b < DBLK; ++b) {
-        const int d = 32 * b + n;
-        dv[b] = mfma32(lds_tr_read(sdOt, d, 4 * qb + g), p0, dv[b]);
-        dv[b] = mfma32(lds_tr_read(sdOt, d, 4 * qb + 2 + g), p1, dv[b]);
-        dk[b] = mfma32(lds_tr_read(sQt, d, 4 * qb + g), d0, dk[b]);
-        dk[b] = mfma32(lds_tr_read(sQt, d, 4 * qb + 2 + g), d1, dk[b]);
+        dv[b] = mfma32(rd.transposed(dot, b, 2 * qb), pk[0], dv[b]);
+        dk[b] = mfma32(rd.transposed(qt, b, 2 * qb), dsk[0], dk[b]);
+        dv[b] = mfma32(rd.transposed(dot, b, 2 * qb + 1), pk[1], dv[b]);
+        dk[b] = mfma32(rd.transposed(qt, b, 2 * qb + 1), dsk[1], dk[b]);
       }
-    }
+    };
+    // The tile's two 32-query blocks; the masked variant is taken only on
+    // diagonal and tail tiles, so the common path carries no mask arithmetic.
+    auto tile_body = [&](auto masked) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        if (CAUSAL && decltype(masked)::value && q0 + 32 * qb + 31 < kw) continue;  // block precedes the keys
+        f32x16 sv, dpv;
+        bf16x8 pk[2], dsk[2];
+        sdp(qb, sv, dpv);
+        grads(masked, qb, sv, dpv, pk, dsk);
+        accumulate(qb, pk, dsk);
+      }
+    };
+    const bool need_mask = (CAUSAL && q0 < kw + 31) || (q0 + kTileRows > N) || (kw + 32 > N);
+    if (need_mask)
+      tile_body(std::integral_constant<bool, true>{});
+    else
+      tile_body(std::integral_constant<bool, false>{});
   }
 
-  if (!wave_live || key >= N) return;
+  if (kw >= N || key >= N) return;
   bf16* dKrow = dK + head_off + (size_t)key * D;
   bf16* dVrow = dV + head_off + (size_t)key * D;
 #pragma unroll
@@ -192,22 +301,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dQ: workgroup = 128 queries of one head; wavefront w owns qw..qw+31.
+// dQ: workgroup = 128 queries of one head; wavefront w owns qw..qw+31 and
+// walks their 64-key tiles (K and V tiles in an LDS ring).  Sᵀ and dPᵀ are
+// held as [key rows x this lane's query] as in the forward; Kᵀ for
+// dQᵀ += Kᵀ dSᵀ is read transposed out of the K tile.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
     bf16* __restrict__ dQ, int N, float scale, float scale_log2) {
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
+  constexpr int TILE = kTileRows * D;
   constexpr int BC = kTileRows;
-  __shared__ __attribute__((aligned(16))) bf16 sK[BC * D];
-  __shared__ __attribute__((aligned(16))) bf16 sKt[D * BC];
-  __shared__ __attribute__((aligned(16))) bf16 sV[BC * D];
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * 2 * TILE];  // [stage][K, V]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
   const int bh = blockIdx.y;
   const int nqb = (N + 127) / 128;
@@ -215,21 +327,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const int q0 = qblk * 128;
   const int qw = q0 + 32 * wave;
   const int qrow = qw + n;
-  const bool wave_live = qw < N;
   const size_t head_off = (size_t)bh * N * D;
-  const bf16* Kh = K + head_off;
-  const bf16* Vh = V + head_off;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto rq = make_rsrc(Q + head_off, head_bytes);
+  const auto rdo = make_rsrc(dO + head_off, head_bytes);
+  const auto rk = make_rsrc(K + head_off, head_bytes);
+  const auto rv = make_rsrc(V + head_off, head_bytes);
 
   bf16x8 qreg[KSTEPS], oreg[KSTEPS];
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
-    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (qrow < N) {
-      x = *reinterpret_cast<const u32x4*>(Q + head_off + (size_t)qrow * D + 16 * kk + 8 * g);
-      y = *reinterpret_cast<const u32x4*>(dO + head_off + (size_t)qrow * D + 16 * kk + 8 * g);
-    }
-    qreg[kk] = __builtin_bit_cast(bf16x8, x);
-    oreg[kk] = __builtin_bit_cast(bf16x8, y);
+    const uint32_t off = (uint32_t)qrow * (D * 2) + (16 * kk + 8 * g) * 2;
+    qreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
+    oreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
   }
   const float lse2 = (qrow < N) ? LSE[(size_t)bh * N + qrow] * kLog2e : 0.f;
   const float dl = (qrow < N) ? delta[(size_t)bh * N + qrow] : 0.f;
@@ -240,62 +350,72 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[b][r] = 0.f;
 
-  const int kv_end = CAUSAL ? min(N, q0 + 128) : N;
-  for (int k0 = 0; k0 < kv_end; k0 += BC) {
-    __syncthreads();
-    {
-      RowTile<D, kThreads> t;
-      t.load(Kh, k0, N, tid);
-      t.store(sK, tid);
-      t.load(Vh, k0, N, tid);
-      t.store(sV, tid);
-      TransTile<D, kThreads> u;
-      u.load(Kh, k0, N, tid);
-      u.store(sKt, tid);
-    }
-    __syncthreads();
-    if (!wave_live || (CAUSAL && k0 > qw + 31)) continue;
-    const bool need_mask = (CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > N) || (qw + 32 > N);
+  TileDma<D> dma;
+  dma.init(wave, lane);
+  TileReads<D> rd;
+  rd.init(lane);
 
+  const int kv_end = CAUSAL ? min(N, q0 + 128) : N;
+  const int ntiles = (kv_end + BC - 1) / BC;
+  const int wnt = (qw >= N) ? 0 : (CAUSAL ? min(ntiles, (min(qw + 31, N - 1) / BC) + 1) : ntiles);
+  auto issue = [&](int t) {
+    bf16* st = smem + (t & 1) * 2 * TILE;
+    dma.issue(rk, st, t * BC);
+    dma.issue(rv, st + TILE, t * BC);
+  };
+  issue(0);
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = t * BC;
+    wait_vm_all();
+    __syncthreads();  // tile t resident; tile t-1 consumed by every wave
+    if (t + 1 < ntiles) issue(t + 1);
+    bf16* kt = smem + (t & 1) * 2 * TILE;
+    bf16* vt = kt + TILE;
+    if (k0 + BC > N) {  // tail: K rows past N must be zero for the transposed product
+      zero_rows<D>(kt, N - k0, tid);
+      __syncthreads();
+    }
+    if (t >= wnt) continue;
+
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = mfma32(rd.row_major(kt, kb, 0), qreg[0], f32x16{});
+      dp[kb] = mfma32(rd.row_major(vt, kb, 0), oreg[0], f32x16{});
+#pragma unroll
+      for (int kk = 1; kk < KSTEPS; ++kk) {
+        s[kb] = mfma32(rd.row_major(kt, kb, kk), qreg[kk], s[kb]);
+        dp[kb] = mfma32(rd.row_major(vt, kb, kk), oreg[kk], dp[kb]);
+      }
+    }
+    const bool need_mask = (CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > N) || (qw + 32 > N);
     bf16x8 dsb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
-      const int row = 32 * kb + perm_row(n);
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        s = mfma32(lds_rm_read<D>(sK, row, 2 * kk + g), qreg[kk], s);
-        dp = mfma32(lds_rm_read<D>(sV, row, 2 * kk + g), oreg[kk], dp);
-      }
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pr = exp2_fast(__builtin_fmaf(s[r], scale_log2, -lse2));
+        const float pr = exp2_fast(__builtin_fmaf(s[kb][r], scale_log2, -lse2));
+        float dsr = pr * (dp[kb][r] - dl);
         if (need_mask) {
           const int ka = k0 + crow(kb, r, g);
           const bool dead = ka >= N || qrow >= N || (CAUSAL && ka > qrow);
-          pr = dead ? 0.f : pr;
+          dsr = dead ? 0.f : dsr;
         }
-        ds[r] = pr * (dp[r] - dl);
+        ds[r] = dsr;
       }
       dsb[2 * kb] = pack8(ds);
       dsb[2 * kb + 1] = pack8(ds + 8);
     }
     // dQᵀ += Kᵀ dSᵀ
 #pragma unroll
-    for (int b = 0; b < DBLK; ++b) {
-      const int d = 32 * b + n;
+    for (int b = 0; b < DBLK; ++b)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) dq[b] = mfma32(lds_tr_read(sKt, d, 2 * kk + g), dsb[kk], dq[b]);
-    }
+      for (int kk = 0; kk < 4; ++kk) dq[b] = mfma32(rd.transposed(kt, b, kk), dsb[kk], dq[b]);
   }
 
-  if (!wave_live || qrow >= N) return;
+  if (qw >= N || qrow >= N) return;
   bf16* row = dQ + head_off + (size_t)qrow * D;
 #pragma unroll
   for (int b = 0; b < DBLK; ++b)

@@ -222,6 +222,17 @@ __device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
 }
 
+// Swizzle for a row-major [64][D] tile that is read both as a row-major MFMA
+// operand (rows perm_row(m) of 16 lanes, one 16-byte chunk each) and through
+// transposed reads (4 consecutive rows x 4 consecutive chunks per 32 lanes):
+// chunk c of row r lives at c ^ dual_swz(r).  The XOR-linear map below keeps
+// both patterns free of bank conflicts for 16- and 32-lane LDS service.
+template <int D>
+__device__ __forceinline__ int dual_swz(int r) {
+  constexpr int b0 = D >= 128 ? 4 : 2, b1 = D >= 128 ? 10 : 4, b2 = 1, b3 = 3;
+  return ((r & 1) ? b0 : 0) ^ ((r & 2) ? b1 : 0) ^ ((r & 4) ? b2 : 0) ^ ((r & 8) ? b3 : 0);
+}
+
 // Key (or query) offset inside a 64-row tile of register r of C block kb, for
 // a lane in half g, when the A rows of the product were read via perm_row().
 __device__ __forceinline__ int crow(int kb, int r, int g) { return 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7); }
