@@ -105,7 +105,7 @@ fa_status fa_backward(fa_dtype dt, int B, int H, int N, int d, const void* q, co
   if (dt != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (B <= 0 || H <= 0 || N < 0 || d <= 0) return FA_ERR_BAD_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if (!fits(B, H, N, d) || (long long)B * H > 65535 ||  // grid.y of the backward kernels
+  if (!fits(B, H, N, d) || (long long)B * H > INT_MAX / 4 ||
       (long long)((N + 63) / 64) * B * H > INT_MAX / 2)
     return FA_ERR_BAD_SHAPE;
   if (!std::isfinite(scale)) return FA_ERR_BAD_SHAPE;

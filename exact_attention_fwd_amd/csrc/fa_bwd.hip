@@ -30,6 +30,20 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Linear block id -> (tile rank, batch*head).  Rank 0 is dispatched first on
+// every XCD (blocks go round-robin over the 8 XCDs, so XCD x runs the ids with
+// id % 8 == x); heads are grouped per XCD so their streamed tiles share L2.
+__device__ __forceinline__ void map_rank(int bid, int BH, int& rank, int& bh) {
+  if ((BH & 7) == 0) {
+    const int xcd = bid & 7, slot = bid >> 3, hpx = BH >> 3;
+    rank = slot / hpx;
+    bh = xcd * hpx + slot % hpx;
+  } else {
+    rank = bid / BH;
+    bh = bid % BH;
+  }
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
@@ -137,7 +151,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
-    bf16* __restrict__ dK, bf16* __restrict__ dV, int N, float scale, float scale_log2) {
+    bf16* __restrict__ dK, bf16* __restrict__ dV, int N, int BH, float scale, float scale_log2) {
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   constexpr int TILE = kTileRows * D;
@@ -148,8 +162,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
-  const int bh = blockIdx.y;
-  const int k0 = blockIdx.x * 128;
+  int rank, bh;
+  map_rank(blockIdx.x, BH, rank, bh);
+  const int k0 = rank * 128;  // causal: the first key tiles see the most queries, so they go first
   const int kw = k0 + 32 * wave;
   const int key = kw + n;  // this lane's key column
   const size_t head_off = (size_t)bh * N * D;
@@ -310,7 +325,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
-    bf16* __restrict__ dQ, int N, float scale, float scale_log2) {
+    bf16* __restrict__ dQ, int N, int BH, float scale, float scale_log2) {
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   constexpr int TILE = kTileRows * D;
@@ -321,9 +336,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
-  const int bh = blockIdx.y;
+  int rank, bh;
+  map_rank(blockIdx.x, BH, rank, bh);
   const int nqb = (N + 127) / 128;
-  const int qblk = CAUSAL ? (nqb - 1 - (int)blockIdx.x) : (int)blockIdx.x;  // heavy tiles first
+  const int qblk = CAUSAL ? (nqb - 1 - rank) : rank;  // causal: the last query tiles see the most keys
   const int q0 = qblk * 128;
   const int qw = q0 + 32 * wave;
   const int qrow = qw + n;
@@ -441,21 +457,21 @@ hipError_t launch(const BackwardArgs& a) {
   auto* k = static_cast<const bf16*>(a.k);
   auto* v = static_cast<const bf16*>(a.v);
   auto* dout = static_cast<const bf16*>(a.dout);
-  const dim3 grid((a.N + 127) / 128, a.BH), block(kThreads);
+  const dim3 grid((unsigned)(((a.N + 127) / 128) * a.BH)), block(kThreads);
   if (a.causal) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), grid, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
-                       static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.N, a.scale, sl2);
+                       static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.N, a.BH, a.scale, sl2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
-                       static_cast<bf16*>(a.dq), a.N, a.scale, sl2);
+                       static_cast<bf16*>(a.dq), a.N, a.BH, a.scale, sl2);
   } else {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), grid, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
-                       static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.N, a.scale, sl2);
+                       static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.N, a.BH, a.scale, sl2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_kernel<D, false>), grid, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
-                       static_cast<bf16*>(a.dq), a.N, a.scale, sl2);
+                       static_cast<bf16*>(a.dq), a.N, a.BH, a.scale, sl2);
   }
   return hipGetLastError();
 }
