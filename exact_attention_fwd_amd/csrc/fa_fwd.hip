@@ -1,18 +1,23 @@
 // Fused exact-attention forward for gfx950.
 //
-// One workgroup owns a tile of 128 queries of one (batch, head); each of its
-// four wavefronts owns 32 of those queries.  Key/value tiles of 64 tokens are
-// streamed through LDS (K row-major, V transposed), and per tile a wave
+// One workgroup owns a tile of 256 queries of one (batch, head); each of its
+// eight wavefronts owns 32 of those queries.  Key/value tiles of 64 tokens
+// stream HBM -> LDS through direct buffer loads into a two-stage ring (K one
+// tile ahead of V), and per tile a wave
 //   1. computes Sᵀ = K·Qᵀ (64 keys x 32 queries) on bf16 MFMA, Q kept in
 //      registers for the whole pass,
 //   2. masks future keys (diagonal tiles only) and keys past N,
-//   3. runs the online softmax: new running max, rescale factor for the old
-//      partial output and normaliser, p = 2^(s·scale·log2e − m),
-//   4. rounds p to bf16 and accumulates Oᵀ += Vᵀ·Pᵀ on MFMA.
-// Holding Sᵀ (one query per lane) keeps every row reduction inside a lane
-// plus one exchange with lane ^ 32, and makes the rescale of O a per-lane
-// scalar.  Only O (bf16, round-to-nearest-even) and the natural-log
-// logsumexp are written back; no score tile ever reaches device memory.
+//   3. runs the online softmax: p = 2^(s·scale·log2e − m) against a running
+//      reference max m that moves (rescaling the partial output and the
+//      normaliser) only when the max grows by more than 2^8,
+//   4. rounds p to bf16 and accumulates Oᵀ += Vᵀ·Pᵀ on MFMA, with Vᵀ read
+//      transposed out of the row-major V tile (ds_read_b64_tr_b16).
+// The scores of tile t+1 are computed on the matrix pipe while the VALU turns
+// tile t into probabilities.  Holding Sᵀ (one query per lane) keeps every row
+// reduction inside a lane plus one exchange with lane ^ 32, and makes the
+// rescale of O a per-lane scalar.  Only O (bf16, round-to-nearest-even) and
+// the natural-log logsumexp are written back; no score tile ever reaches
+// device memory.
 //
 // Method: "Flash Attention 是什么：2026 最新原理、架构演进与实战详解"
 // (ai.lansai.wang), 技术原理 › 核心工作机制 (tiling into on-chip memory and
@@ -25,9 +30,9 @@ namespace fa {
 
 namespace {
 
-constexpr int kBR = 128;  // queries per workgroup
+constexpr int kBR = 256;  // queries per workgroup
 constexpr int kBC = 64;   // keys per tile
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 
 // Map the linear block id to (query tile, batch*head).  Blocks are handed out
