@@ -29,6 +29,8 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "forward",
     "backward",
+    "forward_varlen",
+    "backward_varlen",
     "decode_paged",
     "backward_workspace_bytes",
     "decode_workspace_bytes",
@@ -81,13 +83,17 @@ def _call(rc):
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
             return_lse: bool = True):
-    """Fused forward; returns (o, lse) with lse fp32 [B, H, N] (or None)."""
+    """Fused forward; q [B, H, N, d], k/v [B, Hkv, N, d] (Hkv divides H: grouped
+    key/value heads when Hkv < H).  Returns (o [B, H, N, d], lse fp32 [B, H, N] or None)."""
     torch = _torch()
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must all have shape [B, H, N, d]")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B, H, N, d] and k, v [B, Hkv, N, d]")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d or H % Hkv:
+        raise ValueError("k, v must be [B, Hkv, N, d] with Hkv dividing H")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share a dtype")
-    B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q) if out is None else out
@@ -97,8 +103,41 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
         lse = None
     _check_dev(q, k, v, o, lse)
     with torch.cuda.device(q.device):
-        _call(lib().fa_forward(_dtype_code(q), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                               int(bool(causal)), float(scale), _stream(q)))
+        if Hkv == H:
+            rc = lib().fa_forward(_dtype_code(q), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                  int(bool(causal)), float(scale), _stream(q))
+        else:
+            rc = lib().fa_forward_gqa(_dtype_code(q), B, H, Hkv, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                      int(bool(causal)), float(scale), _stream(q))
+        _call(rc)
+    return o, lse
+
+
+def forward_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, scale: float | None = None,
+                   out=None, lse=None, return_lse: bool = True):
+    """Packed variable-length forward: q [total, H, d], k/v [total, Hkv, d],
+    cu_seqlens int32 [B+1] on the GPU (sequence b = rows cu[b]..cu[b+1]-1).
+    Returns (o [total, H, d], lse fp32 [H, total] or None)."""
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2]:
+        raise ValueError("q must be [total, H, d] and k, v [total, Hkv, d]")
+    if cu_seqlens.dim() != 1 or cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32 [B+1]")
+    total, H, d = q.shape
+    Hkv = k.shape[1]
+    B = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    if not return_lse:
+        lse = None
+    _check_dev(q, k, v, cu_seqlens, o, lse)
+    with torch.cuda.device(q.device):
+        _call(lib().fa_forward_varlen(_dtype_code(q), B, H, Hkv, int(max_seqlen), total, d, _ptr(cu_seqlens), _ptr(q),
+                                      _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(bool(causal)), float(scale),
+                                      _stream(q)))
     return o, lse
 
 
@@ -108,12 +147,13 @@ def backward_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
 
 def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None, workspace=None,
              dq=None, dk=None, dv=None):
-    """Recomputing backward; returns (dq, dk, dv) bf16 [B, H, N, d]."""
+    """Recomputing backward; returns (dq, dk, dv) bf16 with dk, dv shaped like k, v
+    (grouped key/value heads sum their query heads' gradients)."""
     torch = _torch()
     B, H, N, d = q.shape
-    for t in (k, v, o, dout):
-        if t.shape != q.shape:
-            raise ValueError("q, k, v, o, dout must all have shape [B, H, N, d]")
+    Hkv = k.shape[1]
+    if o.shape != q.shape or dout.shape != q.shape or v.shape != k.shape:
+        raise ValueError("o, dout must be shaped like q and v like k")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32:
         raise ValueError("lse must be fp32 [B, H, N]")
     if scale is None:
@@ -125,11 +165,43 @@ def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = 
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check_dev(q, k, v, o, dout, lse, dq, dk, dv, workspace)
+    wsb = workspace.numel() * workspace.element_size()
     with torch.cuda.device(q.device):
-        _call(lib().fa_backward(_dtype_code(q), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
-                                _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                                workspace.numel() * workspace.element_size(), int(bool(causal)), float(scale),
-                                _stream(q)))
+        if Hkv == H:
+            rc = lib().fa_backward(_dtype_code(q), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                   _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), wsb, int(bool(causal)),
+                                   float(scale), _stream(q))
+        else:
+            rc = lib().fa_backward_gqa(_dtype_code(q), B, H, Hkv, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                       _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), wsb,
+                                       int(bool(causal)), float(scale), _stream(q))
+        _call(rc)
+    return dq, dk, dv
+
+
+def backward_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: int, causal: bool = False,
+                    scale: float | None = None, workspace=None, dq=None, dk=None, dv=None):
+    """Backward of forward_varlen (same packed layouts; lse fp32 [H, total])."""
+    torch = _torch()
+    total, H, d = q.shape
+    Hkv = k.shape[1]
+    B = cu_seqlens.numel() - 1
+    if lse.shape != (H, total) or lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32 [H, total]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = int(lib().fa_backward_varlen_workspace_bytes(H, total, d))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_dev(q, k, v, o, dout, lse, cu_seqlens, dq, dk, dv, workspace)
+    with torch.cuda.device(q.device):
+        _call(lib().fa_backward_varlen(_dtype_code(q), B, H, Hkv, int(max_seqlen), total, d, _ptr(cu_seqlens),
+                                       _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                                       _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       int(bool(causal)), float(scale), _stream(q)))
     return dq, dk, dv
 
 

@@ -60,6 +60,20 @@ def _declare(L):
     L.fa_backward.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_size,
                               c_int, c_float, vp]
     L.fa_backward.restype = c_int
+    i32p = vp
+    L.fa_forward_gqa.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, c_int, c_float, vp]
+    L.fa_forward_gqa.restype = c_int
+    L.fa_forward_varlen.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, i32p, vp, vp, vp, vp, vp, c_int,
+                                    c_float, vp]
+    L.fa_forward_varlen.restype = c_int
+    L.fa_backward_gqa.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  c_size, c_int, c_float, vp]
+    L.fa_backward_gqa.restype = c_int
+    L.fa_backward_varlen_workspace_bytes.argtypes = [c_int, c_int, c_int]
+    L.fa_backward_varlen_workspace_bytes.restype = c_size
+    L.fa_backward_varlen.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, i32p, vp, vp, vp, vp, vp, vp,
+                                     vp, vp, vp, vp, c_size, c_int, c_float, vp]
+    L.fa_backward_varlen.restype = c_int
     L.fa_decode_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
     L.fa_decode_workspace_bytes.restype = c_size
     L.fa_decode_paged.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp, c_float, vp,

@@ -5,11 +5,20 @@
 Every .hip file under csrc/ is compiled for gfx950 only and linked into one
 shared library next to this file.  No JIT cache is used: the built library
 lives in the package directory, so it travels with the source tree.
+
+The build fails if any kernel spills vector registers to scratch.  Besides
+the cost of scratch traffic in the hot loops, a spilling build of the dK/dV
+kernel was miscompiled: a spilled 16-byte MFMA operand was reloaded as 12
+bytes into accumulation registers whose fourth register was never written
+(its copy was kept in another register that the reload on that path did
+not read back), which produced NaN gradients.  Keeping every kernel free of
+spills keeps that code path out of the compiler entirely.
 """
 from __future__ import annotations
 
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -31,6 +40,8 @@ HIPCC_FLAGS = [
     "-Wno-unused-function",
     # never emit packed fp32 VALU ops (v_pk_fma/add/mul_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # per-kernel register / LDS / spill report, parsed by _check_resources()
+    "-Rpass-analysis=kernel-resource-usage",
 ]
 
 
@@ -79,16 +90,49 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB_PATH
 
 
+def kernel_resources(text: str):
+    """Parse the kernel-resource-usage remarks: {kernel: {field: value}}."""
+    out, name = {}, None
+    for ln in text.splitlines():
+        if "remark:" not in ln:
+            continue
+        body = ln.split("remark:", 1)[1].split(" [-Rpass", 1)[0].strip()
+        key, _, val = body.partition(":")
+        key, val = key.strip(), val.strip()
+        if key == "Function Name":
+            name = val
+            out[name] = {}
+        elif name is not None and val:
+            out[name][key] = val
+    return out
+
+
+def _check_resources(src, text):
+    res = kernel_resources(text)
+    bad = {k: v for k, v in res.items() if int(v.get("VGPRs Spill", "0")) > 0}
+    if bad:
+        lines = [f"  {k}: {v.get('VGPRs Spill')} VGPRs spilled" for k, v in bad.items()]
+        raise RuntimeError(f"{os.path.basename(src)}: kernels spill vector registers (refused):\n" + "\n".join(lines))
+    return res
+
+
 def _wait(item, verbose):
     src, p = item
     out, _ = p.communicate()
     text = out.decode(errors="replace")
     # hipcc's host pass does not know the packed-fp32 feature name; that note is harmless
-    lines = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln]
+    # (the remarks' source excerpts are the lines starting with "<n> |" or "|")
+    lines = [ln for ln in text.splitlines()
+             if "packed-fp32-ops" not in ln and "remark:" not in ln and not re.match(r"\s*(\d+\s*)?\|", ln)]
     if p.returncode != 0:
         raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n" + "\n".join(lines))
-    if verbose and lines:
-        print("\n".join(lines), flush=True)
+    res = _check_resources(src, text)
+    if verbose:
+        if lines:
+            print("\n".join(lines), flush=True)
+        for k, v in res.items():
+            print(f"  {k[:90]}: VGPR {v.get('VGPRs')} AGPR {v.get('AGPRs')} LDS {v.get('LDS Size [bytes/block]')} "
+                  f"occupancy {v.get('Occupancy [waves/SIMD]')}", flush=True)
 
 
 if __name__ == "__main__":

@@ -44,9 +44,9 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 namespace fa {
 
-size_t backward_workspace_bytes(long long BH, long long N) {
-  if (BH <= 0 || N < 0) return 0;
-  return round256((size_t)BH * (size_t)N * sizeof(float));
+size_t backward_workspace_bytes(long long rows) {
+  if (rows < 0) return 0;
+  return round256((size_t)rows * sizeof(float));
 }
 
 size_t decode_workspace_bytes(long long S, long long H, long long d, long long max_blocks) {
@@ -75,48 +75,109 @@ const char* fa_last_hip_error(void) { return g_last_hip_error; }
 
 int fa_version(void) { return 10000; }
 
+// Checks shared by the dense and packed forms.  `rows_max` is the longest
+// sequence, `stride_rows` the row count a buffer descriptor of one head spans
+// (N for dense, max_seqlen for packed), `row_elems` the elements per row of
+// the widest tensor (d dense, H*d packed).
+static fa_status check_common(int B, int H, int Hkv, int d, long long rows_max, long long row_elems, float scale) {
+  if (B <= 0 || H <= 0 || Hkv <= 0 || d <= 0 || rows_max < 0) return FA_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (H % Hkv != 0) return FA_ERR_BAD_SHAPE;
+  if (!std::isfinite(scale)) return FA_ERR_BAD_SHAPE;
+  if ((long long)B * H > INT_MAX / 4) return FA_ERR_BAD_SHAPE;
+  if ((rows_max + 127) / 128 * (long long)B * H > INT_MAX / 2) return FA_ERR_BAD_SHAPE;
+  if (rows_max * row_elems * 2 >= (1LL << 31)) return FA_ERR_BAD_SHAPE;  // 32-bit buffer offsets per head
+  return FA_OK;
+}
+
+static fa_status forward_impl(fa_dtype dt, fa::AttnShape sh, int d, const void* q, const void* k, const void* v,
+                              void* o, float* lse, int causal, float scale, void* stream) {
+  if (dt != FA_F32 && dt != FA_BF16) return FA_ERR_UNSUPPORTED;
+  const bool packed = sh.cu != nullptr;
+  fa_status st = check_common(sh.B, sh.H, sh.Hkv, d, sh.N, packed ? (long long)sh.H * d : d, scale);
+  if (st != FA_OK) return st;
+  if (packed && sh.total < 0) return FA_ERR_BAD_SHAPE;
+  if (!packed && !fits(sh.B, sh.H, sh.N, d)) return FA_ERR_BAD_SHAPE;
+  if (dt == FA_F32 && (long long)sh.B * sh.H > 65535) return FA_ERR_BAD_SHAPE;  // grid.y limit of the fp32 path
+  if (sh.N == 0 || (packed && sh.total == 0)) return FA_OK;
+  if (!q || !k || !v || !o) return FA_ERR_NULL_PTR;
+  st = device_ready();
+  if (st != FA_OK) return st;
+  fa::ForwardArgs a{dt == FA_BF16, sh, d, q, k, v, o, lse, causal != 0, scale, (hipStream_t)stream};
+  return hip_status(fa::launch_forward(a));
+}
+
 fa_status fa_forward(fa_dtype dt, int B, int H, int N, int d, const void* q, const void* k, const void* v, void* o,
                      float* lse, int causal, float scale, void* stream) {
-  if (dt != FA_F32 && dt != FA_BF16) return FA_ERR_UNSUPPORTED;
-  if (B <= 0 || H <= 0 || N < 0 || d <= 0) return FA_ERR_BAD_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if (!fits(B, H, N, d) || (long long)B * H > INT_MAX / 4 ||
-      (long long)((N + 127) / 128) * B * H > INT_MAX / 2)
-    return FA_ERR_BAD_SHAPE;
-  if (!std::isfinite(scale)) return FA_ERR_BAD_SHAPE;
-  if (dt == FA_F32 && (long long)B * H > 65535) return FA_ERR_BAD_SHAPE;  // grid.y limit of the fp32 path
-  if (N == 0) return FA_OK;
-  if (!q || !k || !v || !o) return FA_ERR_NULL_PTR;
-  fa_status st = device_ready();
-  if (st != FA_OK) return st;
-  fa::ForwardArgs a{dt == FA_BF16, B * H, N, d, q, k, v, o, lse, causal != 0, scale, (hipStream_t)stream};
-  return hip_status(fa::launch_forward(a));
+  return forward_impl(dt, fa::AttnShape{B, H, H, N, 0, nullptr}, d, q, k, v, o, lse, causal, scale, stream);
+}
+
+fa_status fa_forward_gqa(fa_dtype dt, int B, int H, int Hkv, int N, int d, const void* q, const void* k,
+                         const void* v, void* o, float* lse, int causal, float scale, void* stream) {
+  return forward_impl(dt, fa::AttnShape{B, H, Hkv, N, 0, nullptr}, d, q, k, v, o, lse, causal, scale, stream);
+}
+
+fa_status fa_forward_varlen(fa_dtype dt, int B, int H, int Hkv, int max_seqlen, int total, int d,
+                            const int32_t* cu_seqlens, const void* q, const void* k, const void* v, void* o,
+                            float* lse, int causal, float scale, void* stream) {
+  if (!cu_seqlens && B > 0) return FA_ERR_NULL_PTR;
+  return forward_impl(dt, fa::AttnShape{B, H, Hkv, max_seqlen, total, cu_seqlens}, d, q, k, v, o, lse, causal,
+                      scale, stream);
 }
 
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
   (void)d;
-  if (B <= 0 || H <= 0) return 0;
-  return fa::backward_workspace_bytes((long long)B * H, N);
+  if (B <= 0 || H <= 0 || N < 0) return 0;
+  return fa::backward_workspace_bytes((long long)B * H * N);
+}
+
+size_t fa_backward_varlen_workspace_bytes(int H, int total, int d) {
+  (void)d;
+  if (H <= 0 || total < 0) return 0;
+  return fa::backward_workspace_bytes((long long)H * total);
+}
+
+static fa_status backward_impl(fa_dtype dt, fa::AttnShape sh, int d, const void* q, const void* k, const void* v,
+                               const void* o, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, int causal, float scale, void* stream) {
+  if (dt != FA_BF16) return FA_ERR_UNSUPPORTED;
+  const bool packed = sh.cu != nullptr;
+  fa_status st = check_common(sh.B, sh.H, sh.Hkv, d, sh.N, packed ? (long long)sh.H * d : d, scale);
+  if (st != FA_OK) return st;
+  if (packed && sh.total < 0) return FA_ERR_BAD_SHAPE;
+  if (!packed && !fits(sh.B, sh.H, sh.N, d)) return FA_ERR_BAD_SHAPE;
+  if (sh.N == 0 || (packed && sh.total == 0)) return FA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL_PTR;
+  const long long rows = packed ? (long long)sh.H * sh.total : (long long)sh.B * sh.H * sh.N;
+  if (!workspace || workspace_bytes < fa::backward_workspace_bytes(rows)) return FA_ERR_WORKSPACE;
+  st = device_ready();
+  if (st != FA_OK) return st;
+  fa::BackwardArgs a{sh, d, q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace), causal != 0, scale,
+                     (hipStream_t)stream};
+  return hip_status(fa::launch_backward(a));
 }
 
 fa_status fa_backward(fa_dtype dt, int B, int H, int N, int d, const void* q, const void* k, const void* v,
                       const void* o, const void* dout, const float* lse, void* dq, void* dk, void* dv,
                       void* workspace, size_t workspace_bytes, int causal, float scale, void* stream) {
-  if (dt != FA_BF16) return FA_ERR_UNSUPPORTED;
-  if (B <= 0 || H <= 0 || N < 0 || d <= 0) return FA_ERR_BAD_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if (!fits(B, H, N, d) || (long long)B * H > INT_MAX / 4 ||
-      (long long)((N + 63) / 64) * B * H > INT_MAX / 2)
-    return FA_ERR_BAD_SHAPE;
-  if (!std::isfinite(scale)) return FA_ERR_BAD_SHAPE;
-  if (N == 0) return FA_OK;
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL_PTR;
-  if (!workspace || workspace_bytes < fa::backward_workspace_bytes((long long)B * H, N)) return FA_ERR_WORKSPACE;
-  fa_status st = device_ready();
-  if (st != FA_OK) return st;
-  fa::BackwardArgs a{B * H, N, d, q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace),
-                     causal != 0, scale, (hipStream_t)stream};
-  return hip_status(fa::launch_backward(a));
+  return backward_impl(dt, fa::AttnShape{B, H, H, N, 0, nullptr}, d, q, k, v, o, dout, lse, dq, dk, dv, workspace,
+                       workspace_bytes, causal, scale, stream);
+}
+
+fa_status fa_backward_gqa(fa_dtype dt, int B, int H, int Hkv, int N, int d, const void* q, const void* k,
+                          const void* v, const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                          void* dv, void* workspace, size_t workspace_bytes, int causal, float scale, void* stream) {
+  return backward_impl(dt, fa::AttnShape{B, H, Hkv, N, 0, nullptr}, d, q, k, v, o, dout, lse, dq, dk, dv, workspace,
+                       workspace_bytes, causal, scale, stream);
+}
+
+fa_status fa_backward_varlen(fa_dtype dt, int B, int H, int Hkv, int max_seqlen, int total, int d,
+                             const int32_t* cu_seqlens, const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                             size_t workspace_bytes, int causal, float scale, void* stream) {
+  if (!cu_seqlens && B > 0) return FA_ERR_NULL_PTR;
+  return backward_impl(dt, fa::AttnShape{B, H, Hkv, max_seqlen, total, cu_seqlens}, d, q, k, v, o, dout, lse, dq, dk,
+                       dv, workspace, workspace_bytes, causal, scale, stream);
 }
 
 size_t fa_decode_workspace_bytes(int num_seqs, int H, int d, int max_blocks_per_seq) {

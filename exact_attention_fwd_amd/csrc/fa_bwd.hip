@@ -50,9 +50,12 @@ __device__ __forceinline__ float dpp(float x) {
 }
 
 // D_i = dO_i · O_i.  LPR = D/8 lanes share a row, 16 bytes each.
+// Rows are the rows of O/dO in memory order; in the packed layout row j is
+// (token j / H, head j % H) and D_i is stored [H, total] like the LSE.
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const bf16* __restrict__ O, const bf16* __restrict__ dO,
-                                                             float* __restrict__ delta, long long rows) {
+                                                             float* __restrict__ delta, long long rows, int H,
+                                                             long long total, int packed) {
   constexpr int LPR = D / 8;
   constexpr int RPB = kThreads / LPR;  // rows per block pass
   const int c = threadIdx.x % LPR;
@@ -71,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const bf16* __restr
   acc += dpp<0x4E>(acc);
   acc += dpp<0x141>(acc);
   if (LPR == 16) acc += dpp<0x140>(acc);
-  if (row < rows && c == 0) delta[row] = acc;
+  if (row < rows && c == 0) delta[packed ? (row % H) * total + row / H : row] = acc;
 }
 
 // Direct-to-LDS loads of a 64-row tile of a [rows, D] matrix (row-major in
@@ -83,17 +86,20 @@ struct TileDma {
   static constexpr int DPW = kTileRows / RPD / 4;    // blocks per wave
   uint32_t off[DPW];
   int base_blk;
-  __device__ __forceinline__ void init(int wave, int lane) {
+  // `stride`: elements between consecutive rows of the source matrix.
+  __device__ __forceinline__ void init(int wave, int lane, int stride) {
     base_blk = wave * DPW;
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int row = (base_blk + i) * RPD + lane / CPR;
-      off[i] = (uint32_t)row * (D * 2) + (((lane % CPR) ^ dual_swz<D>(row)) << 4);
+      off[i] = (uint32_t)row * (uint32_t)(stride * 2) + (((lane % CPR) ^ dual_swz<D>(row)) << 4);
     }
   }
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, bf16* tile, int row0) const {
+  // rows row0 .. row0+63
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, bf16* tile, int row0, int stride) const {
 #pragma unroll
-    for (int i = 0; i < DPW; ++i) lds_dma16(r, tile + (base_blk + i) * 512, off[i] + (uint32_t)row0 * (D * 2));
+    for (int i = 0; i < DPW; ++i)
+      lds_dma16(r, tile + (base_blk + i) * 512, off[i] + (uint32_t)row0 * (uint32_t)(stride * 2));
   }
 };
 
@@ -151,7 +157,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
-    bf16* __restrict__ dK, bf16* __restrict__ dV, int N, int BH, float scale, float scale_log2) {
+    bf16* __restrict__ dK, bf16* __restrict__ dV, AttnShape shape, float scale, float scale_log2) {
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   constexpr int TILE = kTileRows * D;
@@ -162,25 +168,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
-  int rank, bh;
-  map_rank(blockIdx.x, BH, rank, bh);
+  int rank, bkv;
+  map_rank(blockIdx.x, shape.B * shape.Hkv, rank, bkv);
+  const int b = bkv / shape.Hkv, hkv = bkv % shape.Hkv;
+  const int group = shape.H / shape.Hkv;  // query heads sharing this key/value head
+  const HeadView kv = head_view(shape, b, hkv * group, D);
+  const int N = kv.L;
   const int k0 = rank * 128;  // causal: the first key tiles see the most queries, so they go first
+  if (k0 >= N) return;        // a shorter sequence of a packed batch
   const int kw = k0 + 32 * wave;
   const int key = kw + n;  // this lane's key column
-  const size_t head_off = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto rq = make_rsrc(Q + head_off, head_bytes);
-  const auto rdo = make_rsrc(dO + head_off, head_bytes);
-  const auto rk = make_rsrc(K + head_off, head_bytes);
-  const auto rv = make_rsrc(V + head_off, head_bytes);
-  const float* Lh = LSE + (size_t)bh * N;
-  const float* Dh = delta + (size_t)bh * N;
+  const auto rk = make_rsrc(K + kv.kv_off, (uint32_t)N * kv.kvs * 2);
+  const auto rv = make_rsrc(V + kv.kv_off, (uint32_t)N * kv.kvs * 2);
 
   // Kᵀ and Vᵀ as B operands: lane (g, n) holds row `key`, features 16kk+8g.. (zeros past N).
   bf16x8 kreg[KSTEPS], vreg[KSTEPS];
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
-    const uint32_t off = (uint32_t)key * (D * 2) + (16 * kk + 8 * g) * 2;
+    const uint32_t off = (uint32_t)key * (kv.kvs * 2) + (16 * kk + 8 * g) * 2;
     kreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
     vreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
   }
@@ -193,22 +198,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       dv[b][r] = 0.f;
     }
 
+  const int qstart = CAUSAL ? k0 : 0;  // k0 is a multiple of the 64-query tile
+  const int tph = (N - qstart + kTileRows - 1) / kTileRows;  // query tiles per query head
+  const int ntiles = tph * group;  // the group's query heads one after the other
   TileDma<D> dma;
-  dma.init(wave, lane);
+  dma.init(wave, lane, kv.qs);  // every query head of the group has the same row stride
   TileReads<D> rd;
   rd.init(lane);
-
-  const int qstart = CAUSAL ? k0 : 0;  // k0 is a multiple of the 64-query tile
-  const int ntiles = (N - qstart + kTileRows - 1) / kTileRows;
+  // Query-side addressing of tile i: query head hkv*group + i / tph, rows from qstart + (i % tph)*64.
+  auto qview = [&](int i) { return head_view(shape, b, hkv * group + i / tph, D); };
   auto issue = [&](int i) {
+    const HeadView hq = qview(i);
     bf16* st = smem + (i & 1) * 2 * TILE;
-    dma.issue(rq, st, qstart + i * kTileRows);
-    dma.issue(rdo, st + TILE, qstart + i * kTileRows);
+    const int r0 = qstart + (i % tph) * kTileRows;
+    dma.issue(make_rsrc(Q + hq.q_off, (uint32_t)N * hq.qs * 2), st, r0, hq.qs);
+    dma.issue(make_rsrc(dO + hq.q_off, (uint32_t)N * hq.qs * 2), st + TILE, r0, hq.qs);
   };
   auto load_stat = [&](int i) {  // tid < 64: LSE·log2e, 64 <= tid < 128: D
-    const int q = qstart + i * kTileRows + (tid & 63);
+    const HeadView hq = qview(i);
+    const int q = qstart + (i % tph) * kTileRows + (tid & 63);
     float x = 0.f;
-    if (tid < 128 && q < N) x = (tid < 64) ? Lh[q] * kLog2e : Dh[q];
+    if (tid < 128 && q < N) x = (tid < 64) ? LSE[hq.st_off + q] * kLog2e : delta[hq.st_off + q];
     return x;
   };
   float stat_next = 0.f;
@@ -216,7 +226,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   stat_next = load_stat(0);
 
   for (int i = 0; i < ntiles; ++i) {
-    const int q0 = qstart + i * kTileRows;
+    const int q0 = qstart + (i % tph) * kTileRows;
     const int st = i & 1;
     if (tid < 128) sstat[st][tid >> 6][tid & 63] = stat_next;
     wait_vm_all();
@@ -283,7 +293,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     auto tile_body = [&](auto masked) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        if (CAUSAL && decltype(masked)::value && q0 + 32 * qb + 31 < kw) continue;  // block precedes the keys
+        // masked tiles: skip a 32-query block that precedes the keys (causal) or lies past N
+        if (decltype(masked)::value && (CAUSAL ? q0 + 32 * qb + 31 < kw : q0 + 32 * qb >= N)) continue;
         f32x16 sv, dpv;
         bf16x8 pk[2], dsk[2];
         sdp(qb, sv, dpv);
@@ -299,8 +310,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   }
 
   if (kw >= N || key >= N) return;
-  bf16* dKrow = dK + head_off + (size_t)key * D;
-  bf16* dVrow = dV + head_off + (size_t)key * D;
+  bf16* dKrow = dK + kv.kv_off + (size_t)key * kv.kvs;
+  bf16* dVrow = dV + kv.kv_off + (size_t)key * kv.kvs;
 #pragma unroll
   for (int b = 0; b < DBLK; ++b)
 #pragma unroll
@@ -325,7 +336,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
-    bf16* __restrict__ dQ, int N, int BH, float scale, float scale_log2) {
+    bf16* __restrict__ dQ, AttnShape shape, float scale, float scale_log2) {
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   constexpr int TILE = kTileRows * D;
@@ -337,28 +348,29 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
   int rank, bh;
-  map_rank(blockIdx.x, BH, rank, bh);
-  const int nqb = (N + 127) / 128;
+  map_rank(blockIdx.x, shape.B * shape.H, rank, bh);
+  const HeadView hv = head_view(shape, bh / shape.H, bh % shape.H, D);
+  const int N = hv.L;
+  const int nqb = (shape.N + 127) / 128;
   const int qblk = CAUSAL ? (nqb - 1 - rank) : rank;  // causal: the last query tiles see the most keys
   const int q0 = qblk * 128;
+  if (q0 >= N) return;  // a shorter sequence of a packed batch
   const int qw = q0 + 32 * wave;
   const int qrow = qw + n;
-  const size_t head_off = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto rq = make_rsrc(Q + head_off, head_bytes);
-  const auto rdo = make_rsrc(dO + head_off, head_bytes);
-  const auto rk = make_rsrc(K + head_off, head_bytes);
-  const auto rv = make_rsrc(V + head_off, head_bytes);
+  const auto rq = make_rsrc(Q + hv.q_off, (uint32_t)N * hv.qs * 2);
+  const auto rdo = make_rsrc(dO + hv.q_off, (uint32_t)N * hv.qs * 2);
+  const auto rk = make_rsrc(K + hv.kv_off, (uint32_t)N * hv.kvs * 2);
+  const auto rv = make_rsrc(V + hv.kv_off, (uint32_t)N * hv.kvs * 2);
 
   bf16x8 qreg[KSTEPS], oreg[KSTEPS];
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
-    const uint32_t off = (uint32_t)qrow * (D * 2) + (16 * kk + 8 * g) * 2;
+    const uint32_t off = (uint32_t)qrow * (hv.qs * 2) + (16 * kk + 8 * g) * 2;
     qreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
     oreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
   }
-  const float lse2 = (qrow < N) ? LSE[(size_t)bh * N + qrow] * kLog2e : 0.f;
-  const float dl = (qrow < N) ? delta[(size_t)bh * N + qrow] : 0.f;
+  const float lse2 = (qrow < N) ? LSE[hv.st_off + qrow] * kLog2e : 0.f;
+  const float dl = (qrow < N) ? delta[hv.st_off + qrow] : 0.f;
 
   f32x16 dq[DBLK];
 #pragma unroll
@@ -367,7 +379,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     for (int r = 0; r < 16; ++r) dq[b][r] = 0.f;
 
   TileDma<D> dma;
-  dma.init(wave, lane);
+  dma.init(wave, lane, hv.kvs);
   TileReads<D> rd;
   rd.init(lane);
 
@@ -376,8 +388,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const int wnt = (qw >= N) ? 0 : (CAUSAL ? min(ntiles, (min(qw + 31, N - 1) / BC) + 1) : ntiles);
   auto issue = [&](int t) {
     bf16* st = smem + (t & 1) * 2 * TILE;
-    dma.issue(rk, st, t * BC);
-    dma.issue(rv, st + TILE, t * BC);
+    dma.issue(rk, st, t * BC, hv.kvs);
+    dma.issue(rv, st + TILE, t * BC, hv.kvs);
   };
   issue(0);
 
@@ -432,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   }
 
   if (qw >= N || qrow >= N) return;
-  bf16* row = dQ + head_off + (size_t)qrow * D;
+  bf16* row = dQ + hv.q_off + (size_t)qrow * hv.qs;
 #pragma unroll
   for (int b = 0; b < DBLK; ++b)
 #pragma unroll
@@ -446,10 +458,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
 template <int D>
 hipError_t launch(const BackwardArgs& a) {
-  const long long rows = (long long)a.BH * a.N;
+  const bool packed = a.s.cu != nullptr;
+  const long long rows = packed ? (long long)a.s.total * a.s.H : (long long)a.s.B * a.s.H * a.s.N;
   constexpr int RPB = kThreads / (D / 8);
-  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kThreads), 0, a.stream,
-                     static_cast<const bf16*>(a.o), static_cast<const bf16*>(a.dout), a.delta, rows);
+  if (rows > 0)
+    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kThreads), 0, a.stream,
+                       static_cast<const bf16*>(a.o), static_cast<const bf16*>(a.dout), a.delta, rows, a.s.H,
+                       (long long)a.s.total, packed ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float sl2 = a.scale * kLog2e;
@@ -457,21 +472,22 @@ hipError_t launch(const BackwardArgs& a) {
   auto* k = static_cast<const bf16*>(a.k);
   auto* v = static_cast<const bf16*>(a.v);
   auto* dout = static_cast<const bf16*>(a.dout);
-  const dim3 grid((unsigned)(((a.N + 127) / 128) * a.BH)), block(kThreads);
+  const int tiles = (a.s.N + 127) / 128;
+  const dim3 grid_kv((unsigned)(tiles * a.s.B * a.s.Hkv)), grid_q((unsigned)(tiles * a.s.B * a.s.H)), block(kThreads);
   if (a.causal) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), grid, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
-                       static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.N, a.BH, a.scale, sl2);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), grid_kv, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
+                       static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.s, a.scale, sl2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
-                       static_cast<bf16*>(a.dq), a.N, a.BH, a.scale, sl2);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid_q, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
+                       static_cast<bf16*>(a.dq), a.s, a.scale, sl2);
   } else {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), grid, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
-                       static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.N, a.BH, a.scale, sl2);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), grid_kv, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
+                       static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.s, a.scale, sl2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), grid, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
-                       static_cast<bf16*>(a.dq), a.N, a.BH, a.scale, sl2);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), grid_q, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
+                       static_cast<bf16*>(a.dq), a.s, a.scale, sl2);
   }
   return hipGetLastError();
 }

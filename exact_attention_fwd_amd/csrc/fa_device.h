@@ -74,110 +74,16 @@ __device__ __forceinline__ bf16x8 pack8(const float* p) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// ---------------------------------------------------------------------------
-// LDS tiles of 64 rows.  Two layouts, both in 16-byte chunks XOR-swizzled so
-// that the operand reads of a wavefront are free of bank conflicts:
-//
-//  row-major  [64][D]   (row = token, D contiguous): chunk c of row r lives at
-//                       chunk c ^ rm_swz(r).  Operand reads take rows
-//                       perm_row(m) for lanes m = 0..15, and rm_swz() maps
-//                       those rows to 16 (D=128) / 8 (D=64) distinct chunks.
-//  transposed [D][64]   (row = feature, 64 tokens contiguous, 8 chunks of 8
-//                       tokens): chunk c of row d lives at c ^ tr_swz(d).
-// ---------------------------------------------------------------------------
+// K/V (and Q/dO in the backward) are staged through LDS in tiles of 64 rows.
+constexpr int kTileRows = 64;
+
+// XOR swizzle of the 16-byte chunks of a row-major [64][D] tile read as a
+// row-major MFMA operand: 16 lanes take rows perm_row(m), one chunk each, and
+// rm_swz() maps those rows to 16 (D=128) / 8 (D=64) distinct chunks.
 template <int D>
 __device__ __forceinline__ int rm_swz(int r) {
   return D >= 128 ? (perm_row(r) & 15) : (perm_row(r) & 7);
 }
-__device__ __forceinline__ int tr_swz(int d) { return (d ^ (d >> 3)) & 7; }
-
-constexpr int kTileRows = 64;
-
-// Row-major operand read: 8 consecutive features (16 bytes) of row r, chunk c.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_rm_read(const bf16* tile, int r, int c) {
-  return *reinterpret_cast<const bf16x8*>(tile + r * D + ((c ^ rm_swz<D>(r)) << 3));
-}
-// Transposed operand read: 8 consecutive tokens (chunk c) of feature row d.
-__device__ __forceinline__ bf16x8 lds_tr_read(const bf16* tile, int d, int c) {
-  return *reinterpret_cast<const bf16x8*>(tile + d * kTileRows + ((c ^ tr_swz(d)) << 3));
-}
-
-// Global rows [r0, r0+64) of a [rows, D] bf16 matrix into registers; rows at
-// or past `nrows` read as zero (never touched in memory).
-template <int D, int NT>
-struct RowTile {
-  static constexpr int kChunks = D / 8;
-  static constexpr int kPer = (kTileRows * kChunks + NT - 1) / NT;
-  u32x4 v[kPer];
-
-  __device__ __forceinline__ void load(const bf16* __restrict__ g, int r0, int nrows, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = tid + NT * i;
-      const int r = idx / kChunks, c = idx % kChunks;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (idx < kTileRows * kChunks && r0 + r < nrows)
-        x = *reinterpret_cast<const u32x4*>(g + (size_t)(r0 + r) * D + c * 8);
-      v[i] = x;
-    }
-  }
-  __device__ __forceinline__ void store(bf16* tile, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = tid + NT * i;
-      const int r = idx / kChunks, c = idx % kChunks;
-      if (idx < kTileRows * kChunks)
-        *reinterpret_cast<u32x4*>(tile + r * D + ((c ^ rm_swz<D>(r)) << 3)) = v[i];
-    }
-  }
-};
-
-// Same global rows, stored transposed ([D][64]).  Each work item takes four
-// consecutive rows of one 8-feature chunk and writes eight 4-token pieces.
-template <int D, int NT>
-struct TransTile {
-  static constexpr int kChunks = D / 8;
-  static constexpr int kItems = kChunks * (kTileRows / 4);
-  static constexpr int kPer = (kItems + NT - 1) / NT;
-  u32x4 v[kPer][4];
-
-  __device__ __forceinline__ void load(const bf16* __restrict__ g, int r0, int nrows, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int it = tid + NT * i;
-      const int c = it % kChunks, kg = it / kChunks;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = r0 + 4 * kg + j;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (it < kItems && r < nrows) x = *reinterpret_cast<const u32x4*>(g + (size_t)r * D + c * 8);
-        v[i][j] = x;
-      }
-    }
-  }
-  __device__ __forceinline__ void store(bf16* tile, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int it = tid + NT * i;
-      if (it >= kItems) continue;
-      const int c = it % kChunks, kg = it / kChunks;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a0 = v[i][0][w], a1 = v[i][1][w], a2 = v[i][2][w], a3 = v[i][3][w];
-        // feature 8c+2w: low halves of the four rows; feature 8c+2w+1: high halves
-        u32x2 lo, hi;
-        lo[0] = (a0 & 0xffffu) | (a1 << 16);
-        lo[1] = (a2 & 0xffffu) | (a3 << 16);
-        hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-        hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-        const int d0 = 8 * c + 2 * w, d1 = d0 + 1;
-        *reinterpret_cast<u32x2*>(tile + d0 * kTileRows + (((kg >> 1) ^ tr_swz(d0)) << 3) + ((kg & 1) << 2)) = lo;
-        *reinterpret_cast<u32x2*>(tile + d1 * kTileRows + (((kg >> 1) ^ tr_swz(d1)) << 3) + ((kg & 1) << 2)) = hi;
-      }
-    }
-  }
-};
 
 // ---------------------------------------------------------------------------
 // Buffer resources: 128-bit descriptors over one contiguous byte range.  Raw
@@ -231,6 +137,45 @@ template <int D>
 __device__ __forceinline__ int dual_swz(int r) {
   constexpr int b0 = D >= 128 ? 4 : 2, b1 = D >= 128 ? 10 : 4, b2 = 1, b3 = 3;
   return ((r & 1) ? b0 : 0) ^ ((r & 2) ? b1 : 0) ^ ((r & 4) ? b2 : 0) ^ ((r & 8) ? b3 : 0);
+}
+
+// Addressing of one (batch, query head) unit: element offsets of row 0 in
+// Q/O (and dQ/dO), in K/V (and dK/dV) and in LSE/D, the row strides in
+// elements, and the sequence length.
+struct HeadView {
+  size_t q_off, kv_off, st_off;
+  int L, qs, kvs;
+};
+template <typename Shape>
+__device__ __forceinline__ HeadView head_view(const Shape& s, int b, int h, int D) {
+  HeadView v;
+  const int hkv = h / (s.H / s.Hkv);
+  if (s.cu == nullptr) {
+    v.L = s.N;
+    v.qs = D;
+    v.kvs = D;
+    v.q_off = ((size_t)b * s.H + h) * (size_t)s.N * D;
+    v.kv_off = ((size_t)b * s.Hkv + hkv) * (size_t)s.N * D;
+    v.st_off = ((size_t)b * s.H + h) * (size_t)s.N;
+  } else {
+    // Clamped so that a malformed cu_seqlens can leave rows unwritten but can
+    // never address memory outside [0, total) or past the grid's N rows.
+    const int t0 = min(max(s.cu[b], 0), s.total);
+    const int t1 = min(max(s.cu[b + 1], t0), s.total);
+    v.L = min(t1 - t0, s.N);
+    v.qs = s.H * D;
+    v.kvs = s.Hkv * D;
+    v.q_off = (size_t)t0 * s.H * D + (size_t)h * D;
+    v.kv_off = (size_t)t0 * s.Hkv * D + (size_t)hkv * D;
+    v.st_off = (size_t)h * s.total + t0;
+  }
+  return v;
+}
+// Same addressing for a (batch, key/value head) unit (its K/V rows only).
+template <typename Shape>
+__device__ __forceinline__ HeadView kv_head_view(const Shape& s, int b, int hkv, int D) {
+  HeadView v = head_view(s, b, hkv * (s.H / s.Hkv), D);
+  return v;
 }
 
 // Key (or query) offset inside a 64-row tile of register r of C block kb, for

@@ -75,7 +75,7 @@ constexpr float kRescaleThreshold = 8.0f;
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, float scale_log2) {
+    bf16* __restrict__ O, float* __restrict__ LSE, AttnShape shape, float scale_log2) {
   constexpr int KSTEPS = D / 16;  // MFMA k-steps over the head dim
   constexpr int DBLK = D / 32;    // 32-row output blocks over the head dim
   constexpr int TILE = kTileRows * D;
@@ -92,16 +92,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
-  const int nqb = (N + kBR - 1) / kBR;
+  const int nqb = (shape.N + kBR - 1) / kBR;
   int qb, bh;
-  map_block(blockIdx.x, nqb, BH, CAUSAL, qb, bh);
-
-  const size_t head_off = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto rq = make_rsrc(Q + head_off, head_bytes);
-  const auto rk = make_rsrc(K + head_off, head_bytes);
-  const auto rv = make_rsrc(V + head_off, head_bytes);
+  map_block(blockIdx.x, nqb, shape.B * shape.H, CAUSAL, qb, bh);
+  const HeadView hv = head_view(shape, bh / shape.H, bh % shape.H, D);
+  const int N = hv.L;  // this sequence's length
   const int q0 = qb * kBR;
+  if (q0 >= N) return;  // a shorter sequence of a packed batch: no queries here
+
+  const auto rq = make_rsrc(Q + hv.q_off, (uint32_t)N * hv.qs * 2);
+  const auto rk = make_rsrc(K + hv.kv_off, (uint32_t)N * hv.kvs * 2);
+  const auto rv = make_rsrc(V + hv.kv_off, (uint32_t)N * hv.kvs * 2);
   const int qw = q0 + wave * 32;
   const int qrow = qw + n;  // this lane's query
 
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   bf16x8 qreg[KSTEPS];
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk)
-    qreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)qrow * (D * 2) + (16 * kk + 8 * g) * 2));
+    qreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)qrow * (hv.qs * 2) + (16 * kk + 8 * g) * 2));
 
   // Direct-to-LDS loads: wave w fills 1 KiB blocks w*DMA_PER_WAVE.. of a tile;
   // lane l writes physical chunk l % CPR of row l / CPR of its block, fetching
@@ -119,18 +120,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
   for (int i = 0; i < DMA_PER_WAVE; ++i) {
     const int row = (wave * DMA_PER_WAVE + i) * ROWS_PER_DMA + dma_row;
-    kdma[i] = (uint32_t)row * (D * 2) + ((dma_pc ^ rm_swz<D>(row)) << 4);
-    vdma[i] = (uint32_t)row * (D * 2) + ((dma_pc ^ v_swz<D>(row)) << 4);
+    kdma[i] = (uint32_t)row * (hv.kvs * 2) + ((dma_pc ^ rm_swz<D>(row)) << 4);
+    vdma[i] = (uint32_t)row * (hv.kvs * 2) + ((dma_pc ^ v_swz<D>(row)) << 4);
   }
   auto issue_k = [&](int t) {
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i)
-      lds_dma16(rk, kring + (t & 1) * TILE + (wave * DMA_PER_WAVE + i) * 512, kdma[i] + (uint32_t)t * (64 * D * 2));
+      lds_dma16(rk, kring + (t & 1) * TILE + (wave * DMA_PER_WAVE + i) * 512, kdma[i] + (uint32_t)t * (64 * hv.kvs * 2));
   };
   auto issue_v = [&](int t) {
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i)
-      lds_dma16(rv, vring + (t & 1) * TILE + (wave * DMA_PER_WAVE + i) * 512, vdma[i] + (uint32_t)t * (64 * D * 2));
+      lds_dma16(rv, vring + (t & 1) * TILE + (wave * DMA_PER_WAVE + i) * 512, vdma[i] + (uint32_t)t * (64 * hv.kvs * 2));
   };
 
   // Per-lane LDS element offsets of the operand reads (loop invariant).
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   if (qw >= N || qrow >= N) return;
   const float l_tot = xhalf_sum(l_run);
   const float inv = 1.f / l_tot;
-  bf16* Orow = O + head_off + (size_t)qrow * D;
+  bf16* Orow = O + hv.q_off + (size_t)qrow * hv.qs;
 #pragma unroll
   for (int b = 0; b < DBLK; ++b)
 #pragma unroll
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       w[1] = pack_bf16x2(oacc[b][4 * i + 2] * inv, oacc[b][4 * i + 3] * inv);
       *reinterpret_cast<u32x2*>(Orow + 32 * b + 8 * i + 4 * g) = w;
     }
-  if (LSE != nullptr && g == 0) LSE[(size_t)bh * N + qrow] = (m_run + log2_fast(l_tot)) * kLn2;
+  if (LSE != nullptr && g == 0) LSE[hv.st_off + qrow] = (m_run + log2_fast(l_tot)) * kLn2;
 }
 
 // fp32 path: one thread per query row, keys staged through LDS 32 at a time,
@@ -313,17 +314,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 template <int D>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                      const float* __restrict__ V, float* __restrict__ O,
-                                                     float* __restrict__ LSE, int N, float scale, int causal) {
+                                                     float* __restrict__ LSE, AttnShape shape, float scale,
+                                                     int causal) {
   constexpr int TK = 32;
   __shared__ float sk[TK][D];
   __shared__ float sv[TK][D];
   const int tid = threadIdx.x;
   const int row = blockIdx.x * 64 + tid;
-  const size_t head_off = (size_t)blockIdx.y * N * D;
+  const int bh = blockIdx.y;
+  const HeadView hv = head_view(shape, bh / shape.H, bh % shape.H, D);
+  const int N = hv.L;
+  if ((int)blockIdx.x * 64 >= N) return;
   float q[D], acc[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    q[d] = row < N ? Q[head_off + (size_t)row * D + d] : 0.f;
+    q[d] = row < N ? Q[hv.q_off + (size_t)row * hv.qs + d] : 0.f;
     acc[d] = 0.f;
   }
   float m = kNegInf, l = 0.f;
@@ -333,8 +338,8 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
     for (int i = tid; i < TK * D; i += 64) {
       const int r = i / D, d = i % D;
       const bool ok = k0 + r < N;
-      sk[r][d] = ok ? K[head_off + (size_t)(k0 + r) * D + d] : 0.f;
-      sv[r][d] = ok ? V[head_off + (size_t)(k0 + r) * D + d] : 0.f;
+      sk[r][d] = ok ? K[hv.kv_off + (size_t)(k0 + r) * hv.kvs + d] : 0.f;
+      sv[r][d] = ok ? V[hv.kv_off + (size_t)(k0 + r) * hv.kvs + d] : 0.f;
     }
     __syncthreads();
     for (int j = 0; j < TK; ++j) {
@@ -360,32 +365,32 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
   if (row >= N) return;
   const float inv = 1.f / l;
 #pragma unroll
-  for (int d = 0; d < D; ++d) O[head_off + (size_t)row * D + d] = acc[d] * inv;
-  if (LSE != nullptr) LSE[(size_t)blockIdx.y * N + row] = m + logf(l);
+  for (int d = 0; d < D; ++d) O[hv.q_off + (size_t)row * hv.qs + d] = acc[d] * inv;
+  if (LSE != nullptr) LSE[hv.st_off + row] = m + logf(l);
 }
 
 template <int D>
 hipError_t launch_bf16(const ForwardArgs& a) {
-  const int nqb = (a.N + kBR - 1) / kBR;
-  const dim3 grid(nqb * a.BH), block(kThreads);
+  const int nqb = (a.s.N + kBR - 1) / kBR;
+  const dim3 grid((unsigned)(nqb * a.s.B * a.s.H)), block(kThreads);
   const float sl2 = a.scale * kLog2e;
   auto* q = static_cast<const bf16*>(a.q);
   auto* k = static_cast<const bf16*>(a.k);
   auto* v = static_cast<const bf16*>(a.v);
   auto* o = static_cast<bf16*>(a.o);
   if (a.causal)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.N, a.BH, sl2);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.s, sl2);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.N, a.BH, sl2);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.s, sl2);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_f32(const ForwardArgs& a) {
-  const dim3 grid((a.N + 63) / 64, a.BH), block(64);
+  const dim3 grid((a.s.N + 63) / 64, a.s.B * a.s.H), block(64);
   hipLaunchKernelGGL((fwd_f32_kernel<D>), grid, block, 0, a.stream, static_cast<const float*>(a.q),
                      static_cast<const float*>(a.k), static_cast<const float*>(a.v), static_cast<float*>(a.o),
-                     a.lse, a.N, a.scale, a.causal);
+                     a.lse, a.s, a.scale, a.causal);
   return hipGetLastError();
 }
 

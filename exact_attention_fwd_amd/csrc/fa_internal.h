@@ -8,9 +8,20 @@
 
 namespace fa {
 
+// Shape of an attention problem as the kernels address it.
+//   dense : Q/O [B, H, N, d], K/V [B, Hkv, N, d], LSE/D [B, H, N]
+//   varlen: Q/O [total, H, d], K/V [total, Hkv, d], LSE/D [H, total], sequence
+//           b owning rows cu[b] .. cu[b+1]-1 (cu on the device), N = max length
+// Query head h reads key/value head h / (H / Hkv).
+struct AttnShape {
+  int B, H, Hkv, N, total;
+  const int32_t* cu;  // nullptr: dense
+};
+
 struct ForwardArgs {
   bool bf16;
-  int BH, N, d;
+  AttnShape s;
+  int d;
   const void* q;
   const void* k;
   const void* v;
@@ -22,7 +33,8 @@ struct ForwardArgs {
 };
 
 struct BackwardArgs {
-  int BH, N, d;
+  AttnShape s;
+  int d;
   const void* q;
   const void* k;
   const void* v;
@@ -32,7 +44,7 @@ struct BackwardArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // [BH, N] workspace
+  float* delta;  // D_i, laid out like LSE (workspace)
   int causal;
   float scale;
   hipStream_t stream;
@@ -56,7 +68,7 @@ hipError_t launch_backward(const BackwardArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 
 // Workspace sizes (bytes, rounded up to 256).
-size_t backward_workspace_bytes(long long BH, long long N);
+size_t backward_workspace_bytes(long long rows);  // rows of LSE: B*H*N dense, H*total varlen
 size_t decode_workspace_bytes(long long S, long long H, long long d, long long max_blocks);
 
 }  // namespace fa

@@ -119,6 +119,59 @@ fa_status fa_backward(fa_dtype dt, int B, int H, int N, int d,
                       int causal, float scale, void* stream);
 
 /*
+ * fa_forward_gqa — fa_forward with grouped key/value heads (GQA; MQA when
+ * Hkv == 1): Explainer 进阶学习路径 §4 names the multi-query / grouped-query
+ * adaptation.  q, o: [B, H, N, d]; k, v: [B, Hkv, N, d]; query head h attends
+ * with key/value head h / (H / Hkv).  H must be a multiple of Hkv.  Other
+ * arguments, LSE layout and errors as fa_forward.
+ */
+fa_status fa_forward_gqa(fa_dtype dt, int B, int H, int Hkv, int N, int d,
+                         const void* q, const void* k, const void* v,
+                         void* o, float* lse, int causal, float scale, void* stream);
+
+/*
+ * fa_forward_varlen — a batch of sequences of different lengths packed
+ * without padding (Explainer 使用门槛和条件 §4: per-sample lengths with no
+ * padding waste).
+ *   cu_seqlens  [B+1] int32 on the device: sequence b owns packed rows
+ *               cu_seqlens[b] .. cu_seqlens[b+1]-1; cu_seqlens[0] = 0,
+ *               non-decreasing, cu_seqlens[B] = total.  The table is not
+ *               validated; the kernels clamp each bound to [0, total] and
+ *               each length to max_seqlen, so a malformed table never makes
+ *               them touch memory outside the buffers, but rows it leaves
+ *               uncovered are not written.
+ *   max_seqlen  the largest length (host value; sizes the launch).
+ *   q, o        [total, H, d];  k, v  [total, Hkv, d] (token-major, heads
+ *               interleaved per token).
+ *   lse         [H, total] fp32 or NULL.
+ * Attention (and the causal mask) stays inside each sequence.  dt FA_BF16 or
+ * FA_F32; other arguments and errors as fa_forward_gqa.
+ */
+fa_status fa_forward_varlen(fa_dtype dt, int B, int H, int Hkv, int max_seqlen, int total, int d,
+                            const int32_t* cu_seqlens, const void* q, const void* k, const void* v,
+                            void* o, float* lse, int causal, float scale, void* stream);
+
+/* Backward of fa_forward_gqa: dk, dv are [B, Hkv, N, d] and sum the
+ * gradients of every query head of the group.  Workspace as fa_backward. */
+fa_status fa_backward_gqa(fa_dtype dt, int B, int H, int Hkv, int N, int d,
+                          const void* q, const void* k, const void* v,
+                          const void* o, const void* dout, const float* lse,
+                          void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes,
+                          int causal, float scale, void* stream);
+
+/* Workspace of fa_backward_varlen in bytes: one fp32 per (head, packed row). */
+size_t fa_backward_varlen_workspace_bytes(int H, int total, int d);
+
+/* Backward of fa_forward_varlen (packed layouts as there; lse [H, total]). */
+fa_status fa_backward_varlen(fa_dtype dt, int B, int H, int Hkv, int max_seqlen, int total, int d,
+                             const int32_t* cu_seqlens, const void* q, const void* k, const void* v,
+                             const void* o, const void* dout, const float* lse,
+                             void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes,
+                             int causal, float scale, void* stream);
+
+/*
  * Workspace for fa_decode_paged in bytes: per (sequence, head, KV split) a
  * partial running max, normaliser and unnormalised output row in fp32; a
  * split is half a 256-token page, so at most 2·max_blocks_per_seq splits

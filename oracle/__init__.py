@@ -15,4 +15,8 @@ from .attention import (  # noqa: F401
     attention_backward,
     decode_paged,
     online_forward,
+    attention_forward_gqa,
+    attention_backward_gqa,
+    attention_forward_varlen,
+    attention_backward_varlen,
 )

@@ -22,6 +22,13 @@ What is computed, and where the pages define it:
   cached keys, which live in fixed 256-token pages of a pool reserved up
   front (0539edu.com "Flash不是那个被时代淘汰的插件" §2); a block table maps
   the sequence's logical page b to a physical page.
+* Grouped key/value heads (GQA; MQA when Hkv = 1) — the multi-/grouped-query
+  adaptation the explainer names (进阶学习路径 §4): query head h attends with
+  key/value head h // (H / Hkv); the K/V gradients sum over the group.
+* Packed variable-length batches — the per-sample lengths without padding of
+  the explainer's 使用门槛和条件 §4: sequences concatenated token-major
+  ([total, H, d]), sequence b owning rows cu[b]..cu[b+1]-1, attention (and
+  the causal mask) kept inside each sequence, LSE laid out [H, total].
 * online_forward — the tiled online-softmax recurrence of the explainer's
   关键术语解析 §4 (在线 Softmax: the running max and normaliser update), with
   the partial output rescaled alongside the normaliser and divided by the
@@ -258,3 +265,70 @@ def online_forward(q, k, v, causal=False, scale=None, tile=16):
             o[h] = np.where(l[:, None] > 0, acc / np.where(l > 0, l, 1.0)[:, None], 0.0)
             lse[h] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), NEG_INF)
     return o.reshape(lead + o.shape[-2:]), lse.reshape(lead + lse.shape[-1:])
+
+
+def _expand_kv(x, H):
+    """[B, Hkv, N, d] -> [B, H, N, d]: query head h reads key/value head h // (H/Hkv)."""
+    Hkv = x.shape[1]
+    if H % Hkv:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    return np.repeat(x, H // Hkv, axis=1)
+
+
+def attention_forward_gqa(q, k, v, causal=False, scale=None):
+    """Forward with grouped key/value heads: q [B, H, N, d], k/v [B, Hkv, N, d]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    H = q.shape[1]
+    return attention_forward(q, _expand_kv(k, H), _expand_kv(v, H), causal=causal, scale=scale)
+
+
+def attention_backward_gqa(q, k, v, dout, causal=False, scale=None):
+    """Gradients for grouped key/value heads: dK, dV [B, Hkv, N, d] sum over each group."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    dq, dk, dv = attention_backward(q, _expand_kv(k, H), _expand_kv(v, H), do, causal=causal, scale=scale)
+    g = H // Hkv
+    return dq, dk.reshape(B, Hkv, g, N, -1).sum(axis=2), dv.reshape(B, Hkv, g, N, -1).sum(axis=2)
+
+
+def _unpack(x, t0, t1):
+    """Rows t0..t1-1 of a packed [total, heads, d] tensor as [1, heads, L, d]."""
+    return np.transpose(x[t0:t1], (1, 0, 2))[None]
+
+
+def attention_forward_varlen(q, k, v, cu_seqlens, causal=False, scale=None):
+    """Packed variable-length forward: q [total, H, d], k/v [total, Hkv, d].
+
+    Returns (o [total, H, d], lse [H, total])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu = np.asarray(_f64(cu_seqlens), dtype=np.int64)
+    total, H, d = q.shape
+    o = np.zeros_like(q)
+    lse = np.zeros((H, total))
+    for b in range(len(cu) - 1):
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        if t1 == t0:
+            continue
+        ob, lb = attention_forward_gqa(_unpack(q, t0, t1), _unpack(k, t0, t1), _unpack(v, t0, t1),
+                                       causal=causal, scale=scale)
+        o[t0:t1] = np.transpose(ob[0], (1, 0, 2))
+        lse[:, t0:t1] = lb[0]
+    return o, lse
+
+
+def attention_backward_varlen(q, k, v, dout, cu_seqlens, causal=False, scale=None):
+    """Packed variable-length backward; returns dq [total, H, d], dk, dv [total, Hkv, d]."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
+    cu = np.asarray(_f64(cu_seqlens), dtype=np.int64)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(len(cu) - 1):
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        if t1 == t0:
+            continue
+        gq, gk, gv = attention_backward_gqa(_unpack(q, t0, t1), _unpack(k, t0, t1), _unpack(v, t0, t1),
+                                            _unpack(do, t0, t1), causal=causal, scale=scale)
+        dq[t0:t1] = np.transpose(gq[0], (1, 0, 2))
+        dk[t0:t1] = np.transpose(gk[0], (1, 0, 2))
+        dv[t0:t1] = np.transpose(gv[0], (1, 0, 2))
+    return dq, dk, dv

@@ -118,3 +118,19 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.forward(x, x, x)
+
+
+def test_build_refuses_kernels_that_spill():
+    from exact_attention_fwd_amd import build as b
+    sample = "\n".join([
+        "x.hip:10:1: remark: Function Name: k_ok [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:10:1: remark:     VGPRs: 100 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:10:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:20:1: remark: Function Name: k_spill [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:20:1: remark:     VGPRs Spill: 53 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    res = b.kernel_resources(sample)
+    assert res["k_ok"]["VGPRs"] == "100" and res["k_spill"]["VGPRs Spill"] == "53"
+    with pytest.raises(RuntimeError, match="k_spill"):
+        b._check_resources("x.hip", sample)
+    b._check_resources("x.hip", "\n".join(sample.splitlines()[:3]))

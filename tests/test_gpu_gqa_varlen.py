@@ -1,0 +1,148 @@
+"""GPU parity of grouped key/value heads (GQA/MQA) and packed variable-length
+batches against the fp64 oracle, element by element over every output.
+
+Lengths mix empty, single-token, sub-tile, tile-multiple and multi-tile
+sequences so that every ragged tail and the sequence boundaries inside the
+packed rows are exercised; the group sizes cover MHA (1), GQA (2, 4) and MQA.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.parity import BF16_MAX, BF16_MEAN, F32_MAX, LSE_MAX, check, grouped, to64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X")
+    import exact_attention_fwd_amd  # noqa: F401  (fails loudly if libfa.so is missing)
+    yield
+
+
+def fa():
+    import exact_attention_fwd_amd
+    return exact_attention_fwd_amd
+
+
+def cuda(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+# ---------------------------------------------------------------- GQA / MQA
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,Hkv,N", [(8, 1, 300), (8, 2, 257), (6, 3, 64), (4, 4, 130)])
+def test_gqa_forward_backward(H, Hkv, N, causal, d):
+    q, k, v, do = workloads.gqa_inputs(2, H, Hkv, N, d, "bf16", seed=7 * H + Hkv + N + d, with_dout=True)
+    scale = 1 / math.sqrt(d)
+    print(f"[gqa] B=2 H={H} Hkv={Hkv} N={N} d={d} causal={causal}", flush=True)
+    qd, kd, vd, dod = cuda(q, k, v, do)
+    o, lse = fa().forward(qd, kd, vd, causal=causal)
+    dq, dk, dv = fa().backward(qd, kd, vd, o, dod, lse, causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_forward_gqa(q, k, v, causal=causal, scale=scale)
+    check("gqa O", to64(o), ro, BF16_MAX, BF16_MEAN)
+    check("gqa LSE", to64(lse), rl, LSE_MAX)
+    assert dk.shape == k.shape and dv.shape == v.shape
+    rq, rk, rv = oracle.attention_backward_gqa(q, k, v, do, causal=causal, scale=scale)
+    check("gqa dq", to64(dq), rq, BF16_MAX, BF16_MEAN)
+    g = H // Hkv
+    check("gqa dk", to64(dk), rk, grouped(BF16_MAX, g), grouped(BF16_MEAN, g))
+    check("gqa dv", to64(dv), rv, grouped(BF16_MAX, g), grouped(BF16_MEAN, g))
+
+
+def test_gqa_forward_fp32():
+    q, k, v = workloads.gqa_inputs(1, 4, 2, 77, 64, "f32", seed=5)
+    o, lse = fa().forward(*cuda(q, k, v), causal=True)
+    ro, rl = oracle.attention_forward_gqa(q, k, v, causal=True)
+    check("gqa fp32 O", to64(o), ro, F32_MAX)
+    check("gqa fp32 LSE", to64(lse), rl, LSE_MAX)
+
+
+def test_gqa_rejects_indivisible_heads():
+    q, k, v = cuda(*workloads.gqa_inputs(1, 6, 4, 16, 64, "bf16", seed=1))
+    with pytest.raises(ValueError):
+        fa().forward(q, k, v)
+    # the C ABI itself rejects it too (FA_ERR_BAD_SHAPE)
+    rc = fa().lib().fa_forward_gqa(1, 1, 6, 4, 16, 64, q.data_ptr(), k.data_ptr(), v.data_ptr(), q.data_ptr(), None,
+                                   0, 0.125, None)
+    assert rc == 2
+
+
+# ------------------------------------------------------- packed variable length
+LENS = {
+    "mixed": [300, 0, 1, 64, 129, 7, 513],
+    "one": [1000],
+    "tiny": [1, 1, 2, 0, 3],
+    "tiles": [256, 64, 320],
+}
+
+
+def _varlen_compare(lens, H, Hkv, d, causal, dtype="bf16", with_bwd=True, seed=0):
+    cu, q, k, v, do = workloads.varlen_inputs(lens, H, Hkv, d, dtype, seed=seed, with_dout=True)
+    scale = 1 / math.sqrt(d)
+    mx = max(lens)
+    print(f"[varlen] lens={lens} H={H} Hkv={Hkv} d={d} causal={causal} {dtype}", flush=True)
+    cud, qd, kd, vd, dod = cuda(cu, q, k, v, do)
+    o, lse = fa().forward_varlen(qd, kd, vd, cud, mx, causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_forward_varlen(q, k, v, cu, causal=causal, scale=scale)
+    if dtype == "f32":
+        check("varlen fp32 O", to64(o), ro, F32_MAX)
+    else:
+        check("varlen O", to64(o), ro, BF16_MAX, BF16_MEAN)
+    check("varlen LSE", to64(lse), rl, LSE_MAX)
+    if not with_bwd:
+        return
+    dq, dk, dv = fa().backward_varlen(qd, kd, vd, o, dod, lse, cud, mx, causal=causal)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward_varlen(q, k, v, do, cu, causal=causal, scale=scale)
+    check("varlen dq", to64(dq), rq, BF16_MAX, BF16_MEAN)
+    g = H // Hkv
+    check("varlen dk", to64(dk), rk, grouped(BF16_MAX, g), grouped(BF16_MEAN, g))
+    check("varlen dv", to64(dv), rv, grouped(BF16_MAX, g), grouped(BF16_MEAN, g))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("lens", ["mixed", "one", "tiny", "tiles"])
+def test_varlen_forward_backward(lens, causal, d):
+    _varlen_compare(LENS[lens], 4, 2, d, causal, seed=len(LENS[lens]) + d)
+
+
+def test_varlen_mha_and_mqa():
+    _varlen_compare([200, 33, 0, 700], 4, 4, 128, True, seed=11)
+    _varlen_compare([200, 33, 0, 700], 8, 1, 64, False, seed=12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_forward_fp32(causal):
+    _varlen_compare([90, 0, 1, 40], 2, 1, 64, causal, dtype="f32", with_bwd=False, seed=13)
+
+
+def test_varlen_single_sequence_matches_dense():
+    """One packed sequence is the dense [1, H, N, d] problem in another layout."""
+    cu, q, k, v = workloads.varlen_inputs([777], 4, 4, 128, seed=14)
+    cud, qd, kd, vd = cuda(cu, q, k, v)
+    o, lse = fa().forward_varlen(qd, kd, vd, cud, 777, causal=True)
+    dense = [x.permute(1, 0, 2).unsqueeze(0).contiguous() for x in (qd, kd, vd)]
+    od, lsed = fa().forward(*dense, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, od[0].permute(1, 0, 2))
+    assert torch.equal(lse, lsed[0])
+
+
+def test_varlen_all_empty_is_noop():
+    cu = torch.zeros(4, dtype=torch.int32, device=DEV)
+    z = torch.zeros(0, 2, 64, dtype=torch.bfloat16, device=DEV)
+    o, lse = fa().forward_varlen(z, z, z, cu, 0, causal=True)
+    assert o.shape == (0, 2, 64) and lse.shape == (2, 0)

@@ -153,7 +153,7 @@ def _bwd_compare(name, q, k, v, do, causal, scale, heads=None):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [1, 7, 100, 257, 700])
+@pytest.mark.parametrize("N", [1, 7, 100, 257, 300, 700])
 def test_backward_small(N, causal, d):
     q, k, v, do = workloads.attention_inputs(1, 2, N, d, "bf16", seed=3 * N + d, with_dout=True)
     _bwd_compare(f"bwd N={N} d={d} causal={causal}", q, k, v, do, causal, 1 / math.sqrt(d))

@@ -153,3 +153,28 @@ def workload_inputs(w: Workload, **overrides):
     d = overrides.get("d", w.d)
     return attention_inputs(B, H, N, d, w.dtype, overrides.get("seed", w.seed),
                             with_dout=(w.kind == "bwd"))
+
+
+def gqa_inputs(B, H, Hkv, N, d, dtype="bf16", seed=0, with_dout=False):
+    """Q [B, H, N, d] and K, V [B, Hkv, N, d] (and dO like Q)."""
+    g = _gen(seed)
+    q = _draw(g, (B, H, N, d), dtype)
+    k = _draw(g, (B, Hkv, N, d), dtype)
+    v = _draw(g, (B, Hkv, N, d), dtype)
+    if not with_dout:
+        return q, k, v
+    return q, k, v, _draw(g, (B, H, N, d), dtype)
+
+
+def varlen_inputs(lens, H, Hkv, d, dtype="bf16", seed=0, with_dout=False):
+    """A packed batch: cu_seqlens int32 [B+1], Q [total, H, d], K/V [total, Hkv, d] (and dO)."""
+    g = _gen(seed)
+    lens = [int(x) for x in lens]
+    cu = torch.tensor([0] + list(__import__("itertools").accumulate(lens)), dtype=torch.int32)
+    total = int(cu[-1])
+    q = _draw(g, (total, H, d), dtype)
+    k = _draw(g, (total, Hkv, d), dtype)
+    v = _draw(g, (total, Hkv, d), dtype)
+    if not with_dout:
+        return cu, q, k, v
+    return cu, q, k, v, _draw(g, (total, H, d), dtype)
