@@ -9,7 +9,7 @@ The same JSON line also carries the other configurations of the hot path
 the roofline of the dominant kernel and the CPU oracle timed on a bounded
 sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|bwd|decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|bwd|decode|...]
 """
 from __future__ import annotations
 
@@ -48,8 +48,9 @@ def bwd_flops(B, H, N, d, causal):
 
 def decode_bytes(p):
     S, H, d = p.q.shape
+    Hkv = p.kv_pool.shape[3]
     lens = p.seq_lens.tolist()
-    kv = sum(lens) * H * d * 2 * 2
+    kv = sum(lens) * Hkv * d * 2 * 2  # each valid token's K and V rows, read once
     pages = sum((L + p.page_size - 1) // p.page_size for L in lens)
     return kv + S * H * d * 2 * 2 + S * H * 4 + pages * 4 + S * 4
 
@@ -116,6 +117,59 @@ def bench_forward(cfg, steps, warmup):
             "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def bench_forward_gqa(steps, warmup, Hkv=8):
+    """The 16K causal forward with 32 query heads sharing Hkv key/value heads."""
+    import torch
+    import exact_attention_fwd_amd as fa
+    import workloads
+    w = workloads.CONFIGS["c2a"]
+    q, k, v = (t.to("cuda:0") for t in workloads.gqa_inputs(w.B, w.H, Hkv, w.N, w.d, "bf16", seed=w.seed))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
+    fn = lambda: fa.forward(q, k, v, causal=True, scale=w.scale, out=o, lse=lse)
+    avg, med, total = timed_launches(fn, steps, warmup)
+    fl = fwd_flops(w.B, w.H, w.N, w.d, True)
+    return {"workload": f"fwd_gqa_causal_1x32q{Hkv}kv_16384x128", "kernel": "fwd_bf16_kernel",
+            "flops_per_launch": fl, "avg_ms": avg, "median_ms": med, "tflops": fl / (avg * 1e-3) / 1e12,
+            "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
+VARLEN_SEED = 1010
+
+
+def varlen_lengths():
+    """16 sequence lengths drawn uniform in [256, 8192] (seeded)."""
+    import torch
+    g = torch.Generator().manual_seed(VARLEN_SEED)
+    return torch.randint(256, 8193, (16,), generator=g).tolist()
+
+
+def bench_varlen(steps, warmup, backward=False):
+    """Packed variable-length causal forward (or backward), H=32, d=128."""
+    import torch
+    import exact_attention_fwd_amd as fa
+    import workloads
+    lens = varlen_lengths()
+    H, d = 32, 128
+    cu, q, k, v, do = workloads.varlen_inputs(lens, H, H, d, "bf16", seed=VARLEN_SEED, with_dout=True)
+    cu, q, k, v, do = (t.to("cuda:0") for t in (cu, q, k, v, do))
+    mx = max(lens)
+    o, lse = fa.forward_varlen(q, k, v, cu, mx, causal=True)
+    if backward:
+        ws = torch.empty(int(fa.lib().fa_backward_varlen_workspace_bytes(H, q.shape[0], d)), dtype=torch.uint8,
+                         device="cuda:0")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        fn = lambda: fa.backward_varlen(q, k, v, o, do, lse, cu, mx, causal=True, workspace=ws, dq=dq, dk=dk, dv=dv)
+        fl = sum(bwd_flops(1, H, L, d, True) for L in lens)
+    else:
+        fn = lambda: fa.forward_varlen(q, k, v, cu, mx, causal=True, out=o, lse=lse)
+        fl = sum(fwd_flops(1, H, L, d, True) for L in lens)
+    avg, med, total = timed_launches(fn, steps, warmup)
+    return {"workload": f"{'bwd' if backward else 'fwd'}_varlen_causal_16seq_h32_d128", "seq_lens": lens,
+            "total_tokens": int(sum(lens)), "flops_per_launch": fl, "avg_ms": avg, "median_ms": med,
+            "tflops": fl / (avg * 1e-3) / 1e12, "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def bench_backward(steps, warmup):
     import torch
     import exact_attention_fwd_amd as fa
@@ -133,24 +187,31 @@ def bench_backward(steps, warmup):
             "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-def bench_decode(steps, warmup):
+def bench_decode(steps, warmup, Hkv=None):
+    """Paged decode of the 8-sequence configuration; Hkv < 32 stores that many
+    key/value heads in the pool (grouped-query decode)."""
     import torch
     import exact_attention_fwd_amd as fa
     import workloads
     w = workloads.CONFIGS["c4"]
-    p = workloads.workload_inputs(w)
+    p = workloads.workload_inputs(w, Hkv=Hkv) if Hkv else workloads.workload_inputs(w)
     q, pool, bt, sl = (t.to("cuda:0") for t in (p.q, p.kv_pool, p.block_table, p.seq_lens))
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda:0")
     ws = torch.empty(fa.decode_workspace_bytes(*q.shape, bt.shape[1]), dtype=torch.uint8, device="cuda:0")
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")  # > the 256 MiB last-level cache
+    # Cold K/V: before every call, read 1 GiB (4x the 256 MiB last-level cache).  A read leaves the
+    # caches holding clean lines; a write would leave dirty ones whose write-back lands inside the
+    # timed call.
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
     fn = lambda: fa.decode_paged(q, pool, bt, sl, scale=w.scale, workspace=ws, out=o, lse=lse)
-    avg, med, total = timed_launches(fn, steps, warmup, flush=lambda: scratch.fill_(1))
+    avg, med, total = timed_launches(fn, steps, warmup, flush=lambda: scratch.sum())
     nbytes = decode_bytes(p)
-    return {"workload": w.name, "kernels": "decode_split + decode_merge", "bytes_per_call": nbytes,
-            "seq_lens": p.seq_lens.tolist(), "avg_ms": avg, "median_ms": med,
+    grouped = Hkv is not None and Hkv != w.H
+    return {"workload": w.name + (f"_kv{Hkv}" if grouped else ""),
+            "kernels": "decode_gqa_split + decode_merge" if grouped else "decode_split + decode_merge",
+            "bytes_per_call": nbytes, "seq_lens": p.seq_lens.tolist(), "avg_ms": avg, "median_ms": med,
             "gbs": nbytes / (med * 1e-3) / 1e9, "frac_of_peak": nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "cache": "1 GiB scratch written before every call (cold K/V)"}
+            "cache": "1 GiB scratch read before every call (cold K/V)"}
 
 
 def bench_copy(steps, warmup):
@@ -196,7 +257,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["fwd", "fwd32k", "fwdnc", "fwd4k", "bwd", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "fwd32k", "fwdnc", "fwd4k", "bwd", "decode", "copy", "fwdgqa",
+                                       "fwdvarlen", "bwdvarlen", "decodegqa"], default=None,
                     help="run one path only (for profiler runs); prints its record")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -217,7 +279,11 @@ def main():
                "fwd4k": lambda: bench_forward("c1", args.steps, args.warmup),
                "bwd": lambda: bench_backward(args.steps, args.warmup),
                "copy": lambda: bench_copy(args.steps, args.warmup),
-               "decode": lambda: bench_decode(args.steps, args.warmup)}[args.only]()
+               "decode": lambda: bench_decode(args.steps, args.warmup),
+               "fwdgqa": lambda: bench_forward_gqa(args.steps, args.warmup),
+               "fwdvarlen": lambda: bench_varlen(args.steps, args.warmup),
+               "bwdvarlen": lambda: bench_varlen(args.steps, args.warmup, backward=True),
+               "decodegqa": lambda: bench_decode(args.steps, args.warmup, Hkv=8)}[args.only]()
         print(json.dumps(rec), flush=True)
         return
 
@@ -228,7 +294,11 @@ def main():
                     ("fwd c2b", lambda: bench_forward("c2b", max(5, args.steps // 2), 2)),
                     ("fwd c2c", lambda: bench_forward("c2c", max(5, args.steps // 2), 2)),
                     ("bwd c3", lambda: bench_backward(max(5, args.steps // 2), 2)),
-                    ("decode c4", lambda: bench_decode(args.steps, args.warmup))):
+                    ("decode c4", lambda: bench_decode(args.steps, args.warmup)),
+                    ("fwd gqa 32q/8kv", lambda: bench_forward_gqa(max(5, args.steps // 2), 2)),
+                    ("fwd varlen", lambda: bench_varlen(max(5, args.steps // 2), 2)),
+                    ("bwd varlen", lambda: bench_varlen(max(5, args.steps // 2), 2, backward=True)),
+                    ("decode c4 gqa 32q/8kv", lambda: bench_decode(args.steps, args.warmup, Hkv=8))):
         print(f"# {name}", file=sys.stderr, flush=True)
         secondary.append(f())
         torch.cuda.empty_cache()

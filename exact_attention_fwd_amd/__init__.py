@@ -211,13 +211,14 @@ def decode_workspace_bytes(num_seqs: int, H: int, d: int, max_blocks: int) -> in
 
 def decode_paged(q, kv_pool, block_table, seq_lens, scale: float | None = None, workspace=None, out=None,
                  lse=None, return_lse: bool = True):
-    """Paged decode; q [S, H, d] bf16, kv_pool [P, 2, page, H, d] bf16,
-    block_table [S, max_blocks] int32, seq_lens [S] int32 (all on the GPU).
+    """Paged decode; q [S, H, d] bf16, kv_pool [P, 2, page, Hkv, d] bf16 (Hkv
+    divides H: grouped key/value heads when Hkv < H), block_table
+    [S, max_blocks] int32, seq_lens [S] int32 (all on the GPU).
     Returns (o [S, H, d] bf16, lse [S, H] fp32 or None)."""
     torch = _torch()
     S, H, d = q.shape
-    if kv_pool.dim() != 5 or kv_pool.shape[1] != 2 or kv_pool.shape[3] != H or kv_pool.shape[4] != d:
-        raise ValueError("kv_pool must be [pages, 2, page_size, H, d]")
+    if kv_pool.dim() != 5 or kv_pool.shape[1] != 2 or kv_pool.shape[4] != d or H % kv_pool.shape[3]:
+        raise ValueError("kv_pool must be [pages, 2, page_size, Hkv, d] with Hkv dividing H")
     if block_table.dim() != 2 or block_table.shape[0] != S or block_table.dtype != torch.int32:
         raise ValueError("block_table must be int32 [S, max_blocks]")
     if seq_lens.shape != (S,) or seq_lens.dtype != torch.int32:
@@ -226,7 +227,7 @@ def decode_paged(q, kv_pool, block_table, seq_lens, scale: float | None = None, 
         raise TypeError("paged decode takes bf16 q and kv_pool")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    P, _, page, _, _ = kv_pool.shape
+    P, _, page, Hkv, _ = kv_pool.shape
     mb = block_table.shape[1]
     o = torch.empty_like(q) if out is None else out
     if return_lse and lse is None:
@@ -237,8 +238,15 @@ def decode_paged(q, kv_pool, block_table, seq_lens, scale: float | None = None, 
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check_dev(q, kv_pool, block_table, seq_lens, o, lse, workspace)
+    wsb = workspace.numel() * workspace.element_size()
     with torch.cuda.device(q.device):
-        _call(lib().fa_decode_paged(S, H, d, page, P, mb, _ptr(q), _ptr(kv_pool), _ptr(block_table),
-                                    _ptr(seq_lens), _ptr(o), _ptr(lse), float(scale), _ptr(workspace),
-                                    workspace.numel() * workspace.element_size(), _stream(q)))
+        if Hkv == H:
+            rc = lib().fa_decode_paged(S, H, d, page, P, mb, _ptr(q), _ptr(kv_pool), _ptr(block_table),
+                                       _ptr(seq_lens), _ptr(o), _ptr(lse), float(scale), _ptr(workspace), wsb,
+                                       _stream(q))
+        else:
+            rc = lib().fa_decode_paged_gqa(S, H, Hkv, d, page, P, mb, _ptr(q), _ptr(kv_pool), _ptr(block_table),
+                                           _ptr(seq_lens), _ptr(o), _ptr(lse), float(scale), _ptr(workspace), wsb,
+                                           _stream(q))
+        _call(rc)
     return o, lse

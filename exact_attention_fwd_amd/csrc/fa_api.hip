@@ -83,7 +83,7 @@ static fa_status check_common(int B, int H, int Hkv, int d, long long rows_max, 
   if (B <= 0 || H <= 0 || Hkv <= 0 || d <= 0 || rows_max < 0) return FA_ERR_BAD_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (H % Hkv != 0) return FA_ERR_BAD_SHAPE;
-  if (!std::isfinite(scale)) return FA_ERR_BAD_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_BAD_SHAPE;
   if ((long long)B * H > INT_MAX / 4) return FA_ERR_BAD_SHAPE;
   if ((rows_max + 127) / 128 * (long long)B * H > INT_MAX / 2) return FA_ERR_BAD_SHAPE;
   if (rows_max * row_elems * 2 >= (1LL << 31)) return FA_ERR_BAD_SHAPE;  // 32-bit buffer offsets per head
@@ -184,26 +184,45 @@ size_t fa_decode_workspace_bytes(int num_seqs, int H, int d, int max_blocks_per_
   return fa::decode_workspace_bytes(num_seqs, H, d, max_blocks_per_seq);
 }
 
-fa_status fa_decode_paged(int num_seqs, int H, int d, int page_size, int num_pages, int max_blocks_per_seq,
-                          const void* q, const void* kv_pool, const int32_t* block_table, const int32_t* seq_lens,
-                          void* o, float* lse, float scale, void* workspace, size_t workspace_bytes, void* stream) {
-  if (num_seqs <= 0 || H <= 0 || d <= 0 || page_size <= 0 || num_pages <= 0 || max_blocks_per_seq <= 0)
+static fa_status decode_impl(int num_seqs, int H, int Hkv, int d, int page_size, int num_pages,
+                             int max_blocks_per_seq, const void* q, const void* kv_pool, const int32_t* block_table,
+                             const int32_t* seq_lens, void* o, float* lse, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (num_seqs <= 0 || H <= 0 || Hkv <= 0 || d <= 0 || page_size <= 0 || num_pages <= 0 || max_blocks_per_seq <= 0)
     return FA_ERR_BAD_SHAPE;
+  if (H % Hkv != 0) return FA_ERR_BAD_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (page_size != 256) return FA_ERR_UNSUPPORTED;
-  if (H > 4096 || !fits(num_pages, 2, page_size, (long long)H * d) ||
+  const long long hblocks = (H / Hkv + 31) / 32;  // query-head blocks per key/value head (grouped kernel)
+  if (H > 4096 || !fits(num_pages, 2, page_size, (long long)Hkv * d) ||
       !fits(num_seqs, H, max_blocks_per_seq, d + 2) || (long long)max_blocks_per_seq * page_size > INT_MAX ||
-      (long long)num_seqs * max_blocks_per_seq * 2 * H > INT_MAX)  // grid of the split kernel
+      (long long)num_seqs * max_blocks_per_seq * 2 * H > INT_MAX ||  // grid of the split kernel
+      (long long)num_seqs * max_blocks_per_seq * 2 * Hkv * hblocks > INT_MAX)  // waves of the grouped kernel
     return FA_ERR_BAD_SHAPE;
-  if (!std::isfinite(scale)) return FA_ERR_BAD_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_BAD_SHAPE;
   if (!q || !kv_pool || !block_table || !seq_lens || !o) return FA_ERR_NULL_PTR;
   if (!workspace || workspace_bytes < fa::decode_workspace_bytes(num_seqs, H, d, max_blocks_per_seq))
     return FA_ERR_WORKSPACE;
   fa_status st = device_ready();
   if (st != FA_OK) return st;
-  fa::DecodeArgs a{num_seqs, H, d, page_size, max_blocks_per_seq, q, kv_pool, block_table, seq_lens, o, lse,
-                   scale, static_cast<float*>(workspace), (hipStream_t)stream};
+  fa::DecodeArgs a{num_seqs, H, Hkv, d, page_size, num_pages, max_blocks_per_seq, q, kv_pool, block_table, seq_lens,
+                   o, lse, scale, static_cast<float*>(workspace), (hipStream_t)stream};
   return hip_status(fa::launch_decode(a));
+}
+
+fa_status fa_decode_paged(int num_seqs, int H, int d, int page_size, int num_pages, int max_blocks_per_seq,
+                          const void* q, const void* kv_pool, const int32_t* block_table, const int32_t* seq_lens,
+                          void* o, float* lse, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(num_seqs, H, H, d, page_size, num_pages, max_blocks_per_seq, q, kv_pool, block_table, seq_lens,
+                     o, lse, scale, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_decode_paged_gqa(int num_seqs, int H, int Hkv, int d, int page_size, int num_pages,
+                              int max_blocks_per_seq, const void* q, const void* kv_pool,
+                              const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse, float scale,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(num_seqs, H, Hkv, d, page_size, num_pages, max_blocks_per_seq, q, kv_pool, block_table,
+                     seq_lens, o, lse, scale, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

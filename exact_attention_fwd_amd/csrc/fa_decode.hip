@@ -14,6 +14,18 @@
 // descriptors that end at the sequence's last token, so slots past it are
 // never fetched.  The result per (sequence, head, page) is the partial
 // running max, normaliser and unnormalised output.
+// Kernel 1' (split, grouped key/value heads): the g = H / Hkv query heads
+// that share a key/value head read each K/V row once.  Each wavefront works
+// alone on one (sequence, half page, key/value head, block of up to 32 of its
+// query heads) and streams the half page in 32-token tiles: while tile t is
+// computed, tile t+1's K rows load into registers and its V rows into the
+// wave's LDS ring.  Sᵀ = K·Qᵀ runs on bf16 MFMA with the group's queries as
+// the 32 columns and K read straight into operand registers (16 contiguous
+// bytes of a token row per lane); the per-head online softmax is then a
+// column reduction inside a lane pair, and Oᵀ += Vᵀ·Pᵀ reads Vᵀ transposed out
+// of the ring.  One partial per (sequence, query head, half page).
+// Multi-query / grouped-query sharing of K/V is the adaptation named by
+// "Flash Attention 是什么" (ai.lansai.wang), 进阶学习路径 §4.
 // Kernel 2 (merge): combines the partials of a (sequence, head) exactly:
 // m = max m_b, l = Σ 2^(m_b − m) l_b, O = Σ 2^(m_b − m) õ_b / l — the running
 // max / normaliser update of "Flash Attention 是什么" (ai.lansai.wang),
@@ -57,7 +69,8 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 template <int D, int HG>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ pool, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ seq_lens, float* __restrict__ part, int H, int max_blocks, float scale_log2) {
+    const int32_t* __restrict__ seq_lens, float* __restrict__ part, int H, int num_pages, int max_blocks,
+    float scale_log2) {
   constexpr int LPR = D / 8;                       // lanes per (token, head) row
   constexpr int TP = kDecThreads / (HG * LPR);     // tokens handled side by side
   constexpr int STEPS = kSplit / TP;               // tokens per lane in one split
@@ -76,7 +89,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const int L = seq_lens[s];
   const int ntok = min(kSplit, L - b * kPage - t0);
   if (ntok <= 0) return;  // this split is past the sequence end
-  const int page = block_table[(size_t)s * max_blocks + b];
+  // (a table entry outside the pool is clamped into it: never an access outside the pool)
+  const int page = min(max(block_table[(size_t)s * max_blocks + b], 0), num_pages - 1);
 
   const int tid = threadIdx.x;
   const int c = tid % LPR;
@@ -190,6 +204,198 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   }
 }
 
+// Query heads per wavefront of the grouped kernel (the MFMA's 32 columns).
+constexpr int kGqaCols = 32;
+constexpr int kGqaTokens = 128;  // tokens per wavefront (two partials per page)
+constexpr int kGqaTile = 32;     // tokens per streamed tile
+
+// Wait until at most N vector-memory operations of this wavefront are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int D>
+__global__ __launch_bounds__(kDecThreads, 2) void decode_gqa_split_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ pool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, float* __restrict__ part, int S, int H, int Hkv, int num_pages,
+    int max_blocks, float scale_log2) {
+  constexpr int KSTEPS = D / 16;
+  constexpr int DBLK = D / 32;
+  constexpr int CPR = D / 8;                    // 16-byte chunks per row
+  constexpr int ROWS_PER_DMA = 64 / CPR;        // rows per 1 KiB wavefront load
+  constexpr int NDMA = kGqaTile / ROWS_PER_DMA; // loads per V tile
+  constexpr int VT = kGqaTile * D;              // bf16 elements of one V tile
+  constexpr int SPP = kPage / kGqaTokens;       // partials per page
+  constexpr int kWaves = kDecThreads / 64;
+  __shared__ __attribute__((aligned(1024))) bf16 vring[kWaves][2][VT];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, n = lane & 31;
+  // Wavefront unit = (sequence, split, key/value head, head block), head block
+  // fastest, then key/value head: the waves of a workgroup read neighbouring
+  // rows of the same tokens.
+  const int group = H / Hkv;
+  const int nhb = (group + kGqaCols - 1) / kGqaCols;
+  const int nsplit = max_blocks * SPP;
+  long long unit = (long long)blockIdx.x * kWaves + wave;
+  const int hb = (int)(unit % nhb);
+  unit /= nhb;
+  const int hkv = (int)(unit % Hkv);
+  unit /= Hkv;
+  const int sp = (int)(unit % nsplit);
+  const int s = (int)(unit / nsplit);
+  if (s >= S) return;  // padding of the last workgroup
+  const int b = sp / SPP;                      // logical page
+  const int t0 = (sp % SPP) * kGqaTokens;      // first slot of this split in the page
+  const int ntok = min(kGqaTokens, seq_lens[s] - b * kPage - t0);
+  if (ntok <= 0) return;  // split past the sequence end
+  const int page = min(max(block_table[(size_t)s * max_blocks + b], 0), num_pages - 1);
+  const int cols = min(kGqaCols, group - hb * kGqaCols);  // query heads of this block
+  const int hq0 = hkv * group + hb * kGqaCols;             // its first query head
+
+  // K and V rows of this key/value head over the split's valid tokens only:
+  // a token at or past ntok reads as zero and is never fetched.
+  const uint32_t tok_bytes = (uint32_t)Hkv * D * 2;
+  const bf16* kbase = pool + (size_t)page * 2 * kPage * Hkv * D + (size_t)t0 * Hkv * D + (size_t)hkv * D;
+  const auto rk = make_rsrc(kbase, (uint32_t)ntok * tok_bytes);
+  const auto rv = make_rsrc(kbase + (size_t)kPage * Hkv * D, (uint32_t)ntok * tok_bytes);
+  bf16* ring = &vring[wave][0][0];
+  const int dma_row = lane / CPR, dma_pc = lane % CPR;
+  // Tile t: K rows 32t + perm_row(n) into operand registers, V rows 32t.. into ring slot t & 1.
+  auto issue = [&](int t, bf16x8* kr) {
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      kr[kk] = __builtin_bit_cast(
+          bf16x8, buf_load16_stream(rk, (uint32_t)(kGqaTile * t + perm_row(n)) * tok_bytes + (16 * kk + 8 * g) * 2));
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int row = i * ROWS_PER_DMA + dma_row;
+      lds_dma16(rv, ring + (t & 1) * VT + i * 512,
+                (uint32_t)(kGqaTile * t + row) * tok_bytes + ((dma_pc ^ v_swz<D>(row)) << 4));
+    }
+  };
+
+  // Qᵀ as the B operand: column n is query head hq0 + n (zero past the block's heads).
+  bf16x8 qreg[KSTEPS];
+  {
+    const bf16* qrow = q + ((size_t)s * H + hq0 + min(n, cols - 1)) * D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 16 * kk);
+      qreg[kk] = __builtin_bit_cast(bf16x8, n < cols ? x : z);
+    }
+  }
+  // Transposed V reads: rows 8(G>>1) + j/4 (+16kk), column 32bb + 16(G&1) + 4(j%4).
+  const int G = lane >> 4, j16 = lane & 15;
+  int voff[DBLK];
+#pragma unroll
+  for (int bb = 0; bb < DBLK; ++bb) {
+    const int row = 8 * (G >> 1) + (j16 >> 2);
+    const int col = 32 * bb + 16 * (G & 1) + 4 * (j16 & 3);
+    voff[bb] = row * D + (((col >> 3) ^ v_swz<D>(row)) << 3) + (col & 7);
+  }
+
+  f32x16 oacc[DBLK];
+#pragma unroll
+  for (int bb = 0; bb < DBLK; ++bb) oacc[bb] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+  const int nt = (ntok + kGqaTile - 1) / kGqaTile;
+
+  auto step = [&](int t, const bf16x8* kc, bf16x8* kn) {
+    // Tile t-1's V reads (same ring slot as tile t+1) complete before that slot is refilled.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (t + 1 < nt) issue(t + 1, kn);
+    // Sᵀ (32 tokens x 32 heads); tokens past ntok masked.
+    f32x16 st = mfma32(kc[0], qreg[0], f32x16{});
+#pragma unroll
+    for (int kk = 1; kk < KSTEPS; ++kk) st = mfma32(kc[kk], qreg[kk], st);
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool dead = kGqaTile * t + crow(0, r, g) >= ntok;
+      st[r] = dead ? kNegInf : st[r];
+      mx = fmaxf(mx, st[r]);
+    }
+    mx = xhalf_max(mx) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2_fast(m_run - m_new);  // 0 on the first tile
+      l_run *= alpha;
+#pragma unroll
+      for (int bb = 0; bb < DBLK; ++bb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[bb][r] *= alpha;
+      m_run = m_new;
+    }
+    bf16x8 pb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = exp2_fast(__builtin_fmaf(st[8 * h + 2 * j], scale_log2, -m_run));
+        const float p1 = exp2_fast(__builtin_fmaf(st[8 * h + 2 * j + 1], scale_log2, -m_run));
+        w[j] = pack_bf16x2(p0, p1);
+        l_run += p0 + p1;
+      }
+      pb[h] = __builtin_bit_cast(bf16x8, w);
+    }
+    // V(t) resident: only tile t+1's loads may still be in flight.
+    if (t + 1 < nt)
+      wait_vm<KSTEPS + NDMA>();
+    else
+      wait_vm<0>();
+    bf16* vs = ring + (t & 1) * VT;
+    if (kGqaTile * (t + 1) > ntok) {  // last tile: rows past ntok must read as zero
+      const int first = ntok - kGqaTile * t;
+      for (int idx = lane; idx < (kGqaTile - first) * CPR; idx += 64) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(vs + (first + idx / CPR) * D + (idx % CPR) * 8) = z;
+      }
+    }
+    // Oᵀ += Vᵀ Pᵀ
+#pragma unroll
+    for (int bb = 0; bb < DBLK; ++bb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x4 lo = lds_read_tr4(vs + voff[bb] + 16 * kk * D);
+        const bf16x4 hi = lds_read_tr4(vs + voff[bb] + 16 * kk * D + 4 * D);
+        oacc[bb] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb[kk], oacc[bb]);
+      }
+  };
+
+  bf16x8 ka[KSTEPS], kb2[KSTEPS];
+  issue(0, ka);
+  for (int t = 0; t < nt; t += 2) {  // unrolled by two so the K register buffers alternate
+    step(t, ka, kb2);
+    if (t + 1 < nt) step(t + 1, kb2, ka);
+  }
+
+  // Partial of this split for the block's heads: unnormalised Oᵀ column, max, normaliser.
+  const float l_tot = xhalf_sum(l_run);
+  if (n >= cols) return;
+  float* out = part + (((size_t)s * H + hq0 + n) * nsplit + sp) * (D + 2);
+#pragma unroll
+  for (int bb = 0; bb < DBLK; ++bb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float2 lo, hi;
+      lo.x = oacc[bb][4 * i];
+      lo.y = oacc[bb][4 * i + 1];
+      hi.x = oacc[bb][4 * i + 2];
+      hi.y = oacc[bb][4 * i + 3];
+      *reinterpret_cast<float2*>(out + 32 * bb + 8 * i + 4 * g) = lo;
+      *reinterpret_cast<float2*>(out + 32 * bb + 8 * i + 4 * g + 2) = hi;
+    }
+  if (g == 0) {
+    out[D] = m_run;
+    out[D + 1] = l_tot;
+  }
+}
+
 // One wavefront per (sequence, head): merge the per-split partial states.
 // Lane j holds split j's (m, l); the output features are split over lanes
 // and the splits' rows are loaded in independent batches of eight.
@@ -197,15 +403,23 @@ template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ part,
                                                           const int32_t* __restrict__ seq_lens,
                                                           bf16* __restrict__ O, float* __restrict__ LSE, int H,
-                                                          int max_blocks) {
+                                                          int max_blocks, int split) {
   constexpr int PER = D / 64;
   constexpr int BATCH = 8;
   const int sh = blockIdx.x;
   const int s = sh / H;
   const int lane = threadIdx.x;
-  const int nsplit = max_blocks * kSplitsPerPage;
-  const int ns = (seq_lens[s] + kSplit - 1) / kSplit;
+  const int nsplit = max_blocks * (kPage / split);
+  const int ns = min(max(seq_lens[s], 0), max_blocks * kPage) / split +
+                 (min(max(seq_lens[s], 0), max_blocks * kPage) % split != 0);  // splits that hold tokens
   const float* p = part + (size_t)sh * nsplit * (D + 2);
+  bf16* orow = O + (size_t)sh * D;
+  if (ns == 0) {  // a sequence with no cached token: empty softmax, O = 0 and LSE = -inf
+#pragma unroll
+    for (int e = 0; e < PER; ++e) orow[lane * PER + e] = (bf16)0.f;
+    if (LSE != nullptr && lane == 0) LSE[sh] = kNegInf;
+    return;
+  }
   float m = kNegInf, o[PER], lsum = 0.f;
 #pragma unroll
   for (int e = 0; e < PER; ++e) o[e] = 0.f;
@@ -238,7 +452,6 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
   }
   for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
   const float inv = 1.f / lsum;
-  bf16* orow = O + (size_t)sh * D;
 #pragma unroll
   for (int e = 0; e < PER; ++e) orow[lane * PER + e] = (bf16)(o[e] * inv);
   if (LSE != nullptr && lane == 0) LSE[sh] = (m + log2_fast(lsum)) * kLn2;
@@ -249,18 +462,34 @@ hipError_t launch(const DecodeArgs& a) {
   const int hgroups = a.H / HG;
   const dim3 grid1((unsigned)(a.S * a.max_blocks * kSplitsPerPage * hgroups)), block1(kDecThreads);
   hipLaunchKernelGGL((decode_split_kernel<D, HG>), grid1, block1, 0, a.stream, static_cast<const bf16*>(a.q),
-                     static_cast<const bf16*>(a.kv_pool), a.block_table, a.seq_lens, a.part, a.H, a.max_blocks,
-                     a.scale * kLog2e);
+                     static_cast<const bf16*>(a.kv_pool), a.block_table, a.seq_lens, a.part, a.H, a.num_pages,
+                     a.max_blocks, a.scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.S * a.H), dim3(64), 0, a.stream, a.part, a.seq_lens,
-                     static_cast<bf16*>(a.o), a.lse, a.H, a.max_blocks);
+                     static_cast<bf16*>(a.o), a.lse, a.H, a.max_blocks, kSplit);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_gqa(const DecodeArgs& a) {
+  const long long nhb = (a.H / a.Hkv + kGqaCols - 1) / kGqaCols;
+  const long long units = (long long)a.S * a.max_blocks * (kPage / kGqaTokens) * a.Hkv * nhb;
+  const dim3 grid1((unsigned)((units + kDecThreads / 64 - 1) / (kDecThreads / 64))), block1(kDecThreads);
+  hipLaunchKernelGGL((decode_gqa_split_kernel<D>), grid1, block1, 0, a.stream, static_cast<const bf16*>(a.q),
+                     static_cast<const bf16*>(a.kv_pool), a.block_table, a.seq_lens, a.part, a.S, a.H, a.Hkv,
+                     a.num_pages, a.max_blocks, a.scale * kLog2e);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.S * a.H), dim3(64), 0, a.stream, a.part, a.seq_lens,
+                     static_cast<bf16*>(a.o), a.lse, a.H, a.max_blocks, kGqaTokens);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a) {
+  if (a.Hkv != a.H) return a.d == 128 ? launch_gqa<128>(a) : launch_gqa<64>(a);
   if (a.d == 128) return (a.H % 8 == 0) ? launch<128, 8>(a) : launch<128, 1>(a);
   return (a.H % 8 == 0) ? launch<64, 8>(a) : launch<64, 1>(a);
 }

@@ -85,6 +85,16 @@ __device__ __forceinline__ int rm_swz(int r) {
   return D >= 128 ? (perm_row(r) & 15) : (perm_row(r) & 7);
 }
 
+// Swizzle of the row-major V tile (16-byte chunk c of row r lives at
+// c ^ v_swz(r)).  A transposed operand read covers four consecutive rows per
+// 16-lane group and 16 columns per group pair; the pattern {0, 10, 4, 14} on
+// r % 4 sends those pieces to distinct banks whether the LDS serves 16 or 32
+// lanes of an 8-byte read per cycle.
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  return ((0xE4A0 >> (4 * (row & 3))) & 15) & (D / 8 - 1);
+}
+
 // ---------------------------------------------------------------------------
 // Buffer resources: 128-bit descriptors over one contiguous byte range.  Raw
 // buffer loads past `bytes` return zeros in hardware, so tile loads need no

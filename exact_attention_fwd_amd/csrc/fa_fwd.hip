@@ -56,16 +56,6 @@ __device__ __forceinline__ void map_block(int bid, int nqb, int BH, bool causal,
   bh = head;
 }
 
-// Swizzle of the row-major V tile (16-byte chunk c of row r lives at
-// c ^ v_swz(r)).  A transposed operand read covers four consecutive rows per
-// 16-lane group and 16 columns per group pair; the pattern {0, 10, 4, 14} on
-// r % 4 sends those pieces to distinct banks whether the LDS serves 16 or 32
-// lanes of an 8-byte read per cycle.
-template <int D>
-__device__ __forceinline__ int v_swz(int row) {
-  return ((0xE4A0 >> (4 * (row & 3))) & 15) & (D / 8 - 1);
-}
-
 // Rescale the output only when the running max grows by more than this many
 // powers of two.  Between rescales p = 2^(s·scale·log2e − m) <= 2^8: the
 // output, its normaliser and the logsumexp all use the same reference m, so

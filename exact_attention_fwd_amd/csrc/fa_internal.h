@@ -51,7 +51,7 @@ struct BackwardArgs {
 };
 
 struct DecodeArgs {
-  int S, H, d, page_size, max_blocks;
+  int S, H, Hkv, d, page_size, num_pages, max_blocks;
   const void* q;
   const void* kv_pool;
   const int32_t* block_table;
@@ -59,7 +59,7 @@ struct DecodeArgs {
   void* o;
   float* lse;
   float scale;
-  float* part;  // [S, H, max_blocks, d + 2] fp32 workspace
+  float* part;  // [S, H, splits, d + 2] fp32 workspace (two splits per page, one when Hkv < H)
   hipStream_t stream;
 };
 

@@ -80,7 +80,8 @@ int fa_version(void);
  *           sum over visible keys of exp(scale · q_i·k_j).  It is the only
  *           statistic a recomputing backward needs.
  *   causal  non-zero: query i sees keys 0..i (future keys masked).
- *   scale   softmax scale; callers wanting the usual default pass 1/sqrt(d).
+ *   scale   softmax scale, finite and > 0 (else FA_ERR_BAD_SHAPE); callers
+ *           wanting the usual default pass 1/sqrt(d).
  *           Must be finite.
  * Work: 4·d·pairs·B·H flops, pairs = N(N+1)/2 causal, N² otherwise; extra
  * device memory: none (no N×N buffer).
@@ -198,9 +199,14 @@ size_t fa_decode_workspace_bytes(int num_seqs, int H, int d, int max_blocks_per_
  *   seq_lens            [num_seqs] int32 (device), 1 <= L_s <=
  *                       max_blocks_per_seq·page_size.  Slots >= L_s in the
  *                       last page are never read.
+ * Device-side contents are not validated, but they never make the kernels
+ * touch memory outside the buffers: a table entry outside [0, num_pages) is
+ * clamped into the pool (a wrong page is read), lengths past
+ * max_blocks_per_seq·page_size are cut there, and L_s <= 0 yields O = 0 and
+ * LSE = -inf for that sequence.
  *   o                   [num_seqs, H, d] bf16 (written).
  *   lse                 [num_seqs, H] fp32 (written) or NULL.
- *   scale               softmax scale (finite).
+ *   scale               softmax scale, finite and > 0.
  *   workspace           >= fa_decode_workspace_bytes() bytes, caller-owned.
  * The query sees all L_s cached keys (no causal mask).  Deterministic.
  */
@@ -210,6 +216,25 @@ fa_status fa_decode_paged(int num_seqs, int H, int d, int page_size,
                           const int32_t* block_table, const int32_t* seq_lens,
                           void* o, float* lse, float scale,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_decode_paged_gqa — fa_decode_paged with grouped key/value heads (GQA;
+ * MQA when Hkv == 1): "Flash Attention 是什么" (ai.lansai.wang) 进阶学习路径 §4
+ * names the multi-query / grouped-query adaptation.
+ *   q        [num_seqs, H, d] bf16; query head h reads key/value head
+ *            h / (H / Hkv).  H must be a multiple of Hkv.
+ *   kv_pool  [num_pages, 2, page_size, Hkv, d] bf16.
+ * Each K/V row of the pool is read once for all H / Hkv query heads that
+ * share it.  Workspace: fa_decode_workspace_bytes(num_seqs, H, d,
+ * max_blocks_per_seq) suffices.  Other arguments, outputs and errors as
+ * fa_decode_paged; with Hkv == H it is fa_decode_paged.
+ */
+fa_status fa_decode_paged_gqa(int num_seqs, int H, int Hkv, int d, int page_size,
+                              int num_pages, int max_blocks_per_seq,
+                              const void* q, const void* kv_pool,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              void* o, float* lse, float scale,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -200,23 +200,31 @@ def gather_pages(kv_pool, block_table, seq_len, seq, page_size):
 def decode_paged(q, kv_pool, block_table, seq_lens, scale=None, page_size=256):
     """One query token per sequence over its paged KV cache.
 
-    q [S, H, d]; kv_pool [P, 2, page_size, H, d]; block_table [S, max_blocks];
-    seq_lens [S].  The query sees every one of the sequence's L_s cached keys
-    (its own key is already in the cache), so no causal mask applies.
-    Returns (o [S, H, d], lse [S, H]).
+    q [S, H, d]; kv_pool [P, 2, page_size, Hkv, d] with Hkv dividing H (query
+    head h reads key/value head h // (H // Hkv); Hkv == H is plain multi-head
+    attention); block_table [S, max_blocks]; seq_lens [S].  The query sees
+    every one of the sequence's L_s cached keys (its own key is already in the
+    cache), so no causal mask applies.  A sequence with no cached key has an
+    empty softmax: O = 0 and LSE = -inf.  Returns (o [S, H, d], lse [S, H]).
     """
     q, pool = _f64(q), _f64(kv_pool)
     table = np.asarray(_f64(block_table), dtype=np.int64)
     lens = np.asarray(_f64(seq_lens), dtype=np.int64)
     S, H, d = q.shape
+    Hkv = pool.shape[3]
+    if H % Hkv:
+        raise ValueError("the pool's key/value heads must divide the query heads")
+    group = H // Hkv
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     o = np.zeros((S, H, d))
-    lse = np.zeros((S, H))
+    lse = np.full((S, H), -np.inf)
     for s in range(S):
+        if int(lens[s]) <= 0:
+            continue
         K, V = gather_pages(pool, table, int(lens[s]), s, page_size)
         for h in range(H):
-            oh, lh = _forward_head(q[s, h][None, :], K[:, h], V[:, h], False, scale)
+            oh, lh = _forward_head(q[s, h][None, :], K[:, h // group], V[:, h // group], False, scale)
             o[s, h], lse[s, h] = oh[0], lh[0]
     return o, lse
 

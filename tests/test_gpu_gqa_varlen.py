@@ -146,3 +146,60 @@ def test_varlen_all_empty_is_noop():
     z = torch.zeros(0, 2, 64, dtype=torch.bfloat16, device=DEV)
     o, lse = fa().forward_varlen(z, z, z, cu, 0, causal=True)
     assert o.shape == (0, 2, 64) and lse.shape == (2, 0)
+
+
+# ------------------------------------------------- paged decode, grouped heads
+def _decode_compare(name, p):
+    d = p.q.shape[-1]
+    qd, pool, bt, sl = cuda(p.q, p.kv_pool, p.block_table, p.seq_lens)
+    o, lse = fa().decode_paged(qd, pool, bt, sl)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_paged(p.q, p.kv_pool, p.block_table, p.seq_lens, scale=1 / math.sqrt(d),
+                                 page_size=p.page_size)
+    check(f"{name} O", to64(o), ro, BF16_MAX, BF16_MEAN)
+    check(f"{name} LSE", to64(lse), rl, LSE_MAX)
+    assert torch.isfinite(o.float()).all()
+    return o, lse
+
+
+@pytest.mark.parametrize("Hkv", [1, 4, 8, 16])
+def test_decode_gqa_c4_shape(Hkv):
+    """The paged-decode configuration (8 sequences, 32 query heads, d=128,
+    lengths 1024..8192) with the pool holding Hkv key/value heads, poisoned
+    tails and spare pages."""
+    w = workloads.CONFIGS["c4"]
+    print(f"[decode gqa] H=32 Hkv={Hkv}", flush=True)
+    p = workloads.workload_inputs(w, Hkv=Hkv, poison=True, spare_pages=8)
+    _decode_compare(f"decode H=32 Hkv={Hkv}", p)
+
+
+@pytest.mark.parametrize("H,Hkv,d", [(8, 2, 64), (64, 1, 128), (48, 1, 64), (6, 3, 128)])
+def test_decode_gqa_shapes(H, Hkv, d):
+    lens = [1, 63, 64, 65, 255, 256, 257, 1000]
+    p = workloads.paged_inputs(num_seqs=len(lens), H=H, Hkv=Hkv, d=d, max_blocks=5, seed=H + Hkv + d,
+                               seq_lens=lens, poison=True, spare_pages=3)
+    print(f"[decode gqa] H={H} Hkv={Hkv} d={d}", flush=True)
+    _decode_compare(f"decode H={H} Hkv={Hkv} d={d}", p)
+
+
+def test_decode_gqa_is_deterministic():
+    p = workloads.paged_inputs(num_seqs=4, H=32, Hkv=8, d=128, len_lo=300, len_hi=3000, max_blocks=12, seed=4)
+    args = cuda(p.q, p.kv_pool, p.block_table, p.seq_lens)
+    a = fa().decode_paged(*args)
+    b = fa().decode_paged(*args)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("Hkv", [8, 2])
+def test_decode_empty_sequence(Hkv):
+    """A sequence with no cached token: O = 0 and LSE = -inf, neighbours unaffected."""
+    p = workloads.paged_inputs(num_seqs=3, H=8, Hkv=Hkv, d=128, max_blocks=3, seed=21, seq_lens=[300, 1, 2])
+    p.seq_lens[1] = 0
+    qd, pool, bt, sl = cuda(p.q, p.kv_pool, p.block_table, p.seq_lens)
+    o, lse = fa().decode_paged(qd, pool, bt, sl)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_paged(p.q, p.kv_pool, p.block_table, p.seq_lens, page_size=p.page_size)
+    assert (o[1] == 0).all() and torch.isneginf(lse[1]).all() and np.isneginf(rl[1]).all()
+    keep = [0, 2]
+    check("decode empty neighbours O", to64(o)[keep], ro[keep], BF16_MAX, BF16_MEAN)
+    check("decode empty neighbours LSE", to64(lse)[keep], rl[keep], LSE_MAX)

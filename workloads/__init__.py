@@ -89,7 +89,7 @@ def attention_inputs(B, H, N, d, dtype="bf16", seed=0, with_dout=False):
 @dataclass
 class PagedInputs:
     q: torch.Tensor            # [S, H, d] bf16
-    kv_pool: torch.Tensor      # [P, 2, page, H, d] bf16
+    kv_pool: torch.Tensor      # [P, 2, page, Hkv, d] bf16
     block_table: torch.Tensor  # [S, max_blocks] int32, -1 past the last page
     seq_lens: torch.Tensor     # [S] int32
     page_size: int
@@ -98,8 +98,8 @@ class PagedInputs:
 
 def paged_inputs(num_seqs=8, H=32, d=128, len_lo=1024, len_hi=8192, max_blocks=32,
                  seed=0, page_size=PAGE_SIZE, poison=False, spare_pages=0,
-                 seq_lens=None):
-    """Draw a paged KV cache.
+                 seq_lens=None, Hkv=None):
+    """Draw a paged KV cache (pool [P, 2, page, Hkv, d], Hkv = H unless given).
 
     Lengths are uniform integers in [len_lo, len_hi] (or given); each sequence
     takes ceil(L/page) pages; the physical page ids are a random permutation of
@@ -122,7 +122,7 @@ def paged_inputs(num_seqs=8, H=32, d=128, len_lo=1024, len_hi=8192, max_blocks=3
     total = used + spare_pages
     perm = torch.randperm(total, generator=g)
     q = _draw(g, (num_seqs, H, d), "bf16")
-    pool = _draw(g, (total, 2, page_size, H, d), "bf16")
+    pool = _draw(g, (total, 2, page_size, H if Hkv is None else Hkv, d), "bf16")
     table = torch.full((num_seqs, max_blocks), -1, dtype=torch.int32)
     off = 0
     for s, p in enumerate(pages):
