@@ -30,18 +30,24 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Linear block id -> (tile rank, batch*head).  Rank 0 is dispatched first on
-// every XCD (blocks go round-robin over the 8 XCDs, so XCD x runs the ids with
-// id % 8 == x); heads are grouped per XCD so their streamed tiles share L2.
-__device__ __forceinline__ void map_rank(int bid, int BH, int& rank, int& bh) {
+// Linear block id -> (tile rank, batch entry, head).  Blocks go round-robin
+// over the 8 XCDs (XCD x runs the ids with id % 8 == x).  Units are numbered
+// head-major (u = h·B + b) and each XCD takes a contiguous range of them, so
+// a head's streamed tiles share that XCD's L2 and uneven sequence lengths of
+// a packed batch spread over all XCDs; rank 0 is dispatched first.
+__device__ __forceinline__ void map_unit(int bid, int B, int H, int& rank, int& b, int& h) {
+  const int BH = B * H;
+  int u;
   if ((BH & 7) == 0) {
-    const int xcd = bid & 7, slot = bid >> 3, hpx = BH >> 3;
-    rank = slot / hpx;
-    bh = xcd * hpx + slot % hpx;
+    const int xcd = bid & 7, slot = bid >> 3, upx = BH >> 3;
+    rank = slot / upx;
+    u = xcd * upx + slot % upx;
   } else {
     rank = bid / BH;
-    bh = bid % BH;
+    u = bid % BH;
   }
+  b = u % B;
+  h = u / B;
 }
 
 template <int CTRL>
@@ -168,9 +174,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
-  int rank, bkv;
-  map_rank(blockIdx.x, shape.B * shape.Hkv, rank, bkv);
-  const int b = bkv / shape.Hkv, hkv = bkv % shape.Hkv;
+  int rank, b, hkv;
+  map_unit(blockIdx.x, shape.B, shape.Hkv, rank, b, hkv);
   const int group = shape.H / shape.Hkv;  // query heads sharing this key/value head
   const HeadView kv = head_view(shape, b, hkv * group, D);
   const int N = kv.L;
@@ -347,14 +352,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
-  int rank, bh;
-  map_rank(blockIdx.x, shape.B * shape.H, rank, bh);
-  const HeadView hv = head_view(shape, bh / shape.H, bh % shape.H, D);
+  int rank, bi, hi;
+  map_unit(blockIdx.x, shape.B, shape.H, rank, bi, hi);
+  const HeadView hv = head_view(shape, bi, hi, D);
   const int N = hv.L;
-  const int nqb = (shape.N + 127) / 128;
+  const int nqb = (N + 127) / 128;
+  if (rank >= nqb) return;  // a shorter sequence of a packed batch
   const int qblk = CAUSAL ? (nqb - 1 - rank) : rank;  // causal: the last query tiles see the most keys
   const int q0 = qblk * 128;
-  if (q0 >= N) return;  // a shorter sequence of a packed batch
   const int qw = q0 + 32 * wave;
   const int qrow = qw + n;
   const auto rq = make_rsrc(Q + hv.q_off, (uint32_t)N * hv.qs * 2);

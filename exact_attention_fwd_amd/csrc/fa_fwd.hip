@@ -35,25 +35,28 @@ constexpr int kBC = 64;   // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 
-// Map the linear block id to (query tile, batch*head).  Blocks are handed out
-// round-robin over the 8 XCDs, so the ids of one XCD are bid % 8 == x.  Heads
-// are grouped per XCD (their K/V then share that XCD's L2), and within an
-// XCD the query tiles with the most work (causal: the last ones) go first.
-__device__ __forceinline__ void map_block(int bid, int nqb, int BH, bool causal, int& qb, int& bh) {
-  const int total = nqb * BH;
-  int rank, head;
+// Map the linear block id to (tile rank, batch entry, head).  Blocks are
+// handed out round-robin over the 8 XCDs, so the ids of one XCD are
+// bid % 8 == x.  Units are numbered head-major (u = h·B + b), and each XCD
+// takes a contiguous range of them: whole heads across every batch entry, so
+// uneven sequence lengths of a packed batch spread over all XCDs, and heads
+// that share key/value rows (grouped heads are consecutive) share an L2.
+// Within an XCD the tile ranks go in order; the caller turns rank 0 into the
+// heaviest tile of its own sequence.
+__device__ __forceinline__ void map_unit(int bid, int B, int H, int& rank, int& b, int& h) {
+  const int BH = B * H;
+  int u;
   if ((BH & 7) == 0) {
     const int xcd = bid & 7, slot = bid >> 3;
-    const int hpx = BH >> 3;
-    rank = slot / hpx;
-    head = xcd * hpx + slot % hpx;
+    const int upx = BH >> 3;
+    rank = slot / upx;
+    u = xcd * upx + slot % upx;
   } else {
     rank = bid / BH;
-    head = bid % BH;
+    u = bid % BH;
   }
-  (void)total;
-  qb = causal ? (nqb - 1 - rank) : rank;
-  bh = head;
+  b = u % B;
+  h = u / B;
 }
 
 // Rescale the output only when the running max grows by more than this many
@@ -82,13 +85,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
-  const int nqb = (shape.N + kBR - 1) / kBR;
-  int qb, bh;
-  map_block(blockIdx.x, nqb, shape.B * shape.H, CAUSAL, qb, bh);
-  const HeadView hv = head_view(shape, bh / shape.H, bh % shape.H, D);
+  int rank, bi, hi;
+  map_unit(blockIdx.x, shape.B, shape.H, rank, bi, hi);
+  const HeadView hv = head_view(shape, bi, hi, D);
   const int N = hv.L;  // this sequence's length
+  const int nqb = (N + kBR - 1) / kBR;
+  if (rank >= nqb) return;  // a shorter sequence of a packed batch: no tile of this rank
+  const int qb = CAUSAL ? nqb - 1 - rank : rank;  // causal: the last query tiles see the most keys
   const int q0 = qb * kBR;
-  if (q0 >= N) return;  // a shorter sequence of a packed batch: no queries here
 
   const auto rq = make_rsrc(Q + hv.q_off, (uint32_t)N * hv.qs * 2);
   const auto rk = make_rsrc(K + hv.kv_off, (uint32_t)N * hv.kvs * 2);
