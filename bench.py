@@ -170,6 +170,38 @@ def bench_varlen(steps, warmup, backward=False):
             "tflops": fl / (avg * 1e-3) / 1e12, "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
+PREFILL_SEED = 1020
+
+
+def prefill_shapes():
+    """8 sequences, each a 2048-token chunk appended to a cached prefix drawn
+    uniform in [0, 6144] tokens (seeded)."""
+    import torch
+    g = torch.Generator().manual_seed(PREFILL_SEED)
+    prefix = torch.randint(0, 6145, (8,), generator=g).tolist()
+    return [2048] * 8, [p + 2048 for p in prefix]
+
+
+def bench_prefill(steps, warmup, Hkv=8):
+    """Causal chunked prefill through the paged pool, H=32 query heads, d=128."""
+    import exact_attention_fwd_amd as fa
+    import workloads
+    chunks, ctx = prefill_shapes()
+    H, d = 32, 128
+    p = workloads.prefill_inputs(chunks, ctx, H=H, Hkv=Hkv, d=d, seed=PREFILL_SEED)
+    q, pool, bt, sl, cu = (t.to("cuda:0") for t in (p.q, p.kv_pool, p.block_table, p.seq_lens_k,
+                                                    p.cu_seqlens_q))
+    o, lse = fa.prefill_paged(q, pool, bt, sl, cu, max(chunks), causal=True)
+    fn = lambda: fa.prefill_paged(q, pool, bt, sl, cu, max(chunks), causal=True, out=o, lse=lse)
+    avg, med, total = timed_launches(fn, steps, warmup)
+    # visible (query, key) pairs: query i of a chunk of n over L keys sees i + L - n + 1
+    vis = sum(n * (L - n) + n * (n + 1) // 2 for n, L in zip(chunks, ctx))
+    fl = 4.0 * d * H * vis
+    return {"workload": f"prefill_paged_causal_8x2048_h32_kv{Hkv}_d128", "chunks": chunks, "cached_keys": ctx,
+            "flops_per_launch": fl, "avg_ms": avg, "median_ms": med, "tflops": fl / (avg * 1e-3) / 1e12,
+            "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def bench_backward(steps, warmup):
     import torch
     import exact_attention_fwd_amd as fa
@@ -258,7 +290,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["fwd", "fwd32k", "fwdnc", "fwd4k", "bwd", "decode", "copy", "fwdgqa",
-                                       "fwdvarlen", "bwdvarlen", "decodegqa"], default=None,
+                                       "fwdvarlen", "bwdvarlen", "decodegqa", "prefill"], default=None,
                     help="run one path only (for profiler runs); prints its record")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -283,7 +315,8 @@ def main():
                "fwdgqa": lambda: bench_forward_gqa(args.steps, args.warmup),
                "fwdvarlen": lambda: bench_varlen(args.steps, args.warmup),
                "bwdvarlen": lambda: bench_varlen(args.steps, args.warmup, backward=True),
-               "decodegqa": lambda: bench_decode(args.steps, args.warmup, Hkv=8)}[args.only]()
+               "decodegqa": lambda: bench_decode(args.steps, args.warmup, Hkv=8),
+               "prefill": lambda: bench_prefill(args.steps, args.warmup)}[args.only]()
         print(json.dumps(rec), flush=True)
         return
 
@@ -298,7 +331,8 @@ def main():
                     ("fwd gqa 32q/8kv", lambda: bench_forward_gqa(max(5, args.steps // 2), 2)),
                     ("fwd varlen", lambda: bench_varlen(max(5, args.steps // 2), 2)),
                     ("bwd varlen", lambda: bench_varlen(max(5, args.steps // 2), 2, backward=True)),
-                    ("decode c4 gqa 32q/8kv", lambda: bench_decode(args.steps, args.warmup, Hkv=8))):
+                    ("decode c4 gqa 32q/8kv", lambda: bench_decode(args.steps, args.warmup, Hkv=8)),
+                    ("prefill paged", lambda: bench_prefill(max(5, args.steps // 2), 2))):
         print(f"# {name}", file=sys.stderr, flush=True)
         secondary.append(f())
         torch.cuda.empty_cache()

@@ -9,6 +9,7 @@ fails, a RuntimeError is raised.
     o, lse = forward(q, k, v, causal=True)            # q,k,v [B,H,N,d] bf16/fp32
     dq, dk, dv = backward(q, k, v, o, do, lse, causal=True)
     o, lse = decode_paged(q, kv_pool, block_table, seq_lens)
+    o, lse = prefill_paged(q, kv_pool, block_table, seq_lens, cu_seqlens_q, max_q)
 
 The softmax scale defaults to 1/sqrt(d), the default of the explainer pages
 (lqnn.cn "为什么Flash突然成了AI圈的高频词" §3.3).
@@ -32,6 +33,7 @@ __all__ = [
     "forward_varlen",
     "backward_varlen",
     "decode_paged",
+    "prefill_paged",
     "backward_workspace_bytes",
     "decode_workspace_bytes",
     "FaError",
@@ -249,4 +251,42 @@ def decode_paged(q, kv_pool, block_table, seq_lens, scale: float | None = None, 
                                            _ptr(seq_lens), _ptr(o), _ptr(lse), float(scale), _ptr(workspace), wsb,
                                            _stream(q))
         _call(rc)
+    return o, lse
+
+
+def prefill_paged(q, kv_pool, block_table, seq_lens_k, cu_seqlens_q, max_seqlen_q: int, causal: bool = True,
+                  scale: float | None = None, out=None, lse=None, return_lse: bool = True):
+    """Chunked prefill over a paged KV cache: q [total_q, H, d] bf16 (the new
+    chunk of every sequence, packed by cu_seqlens_q int32 [B+1]); kv_pool
+    [P, 2, page, Hkv, d] bf16 holding each sequence's seq_lens_k[b] keys
+    (prefix, then the chunk) through block_table [B, max_blocks] int32.
+    Causal: query i of a chunk of n sees keys 0 .. i + seq_lens_k[b] - n.
+    Returns (o [total_q, H, d] bf16, lse [H, total_q] fp32 or None)."""
+    torch = _torch()
+    if q.dim() != 3 or kv_pool.dim() != 5 or kv_pool.shape[1] != 2 or kv_pool.shape[4] != q.shape[2]:
+        raise ValueError("q must be [total_q, H, d] and kv_pool [pages, 2, page_size, Hkv, d]")
+    total, H, d = q.shape
+    P, _, page, Hkv, _ = kv_pool.shape
+    B = cu_seqlens_q.numel() - 1
+    if H % Hkv:
+        raise ValueError("the pool's key/value heads must divide the query heads")
+    if cu_seqlens_q.dtype != torch.int32 or seq_lens_k.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise ValueError("cu_seqlens_q, seq_lens_k and block_table must be int32")
+    if seq_lens_k.shape != (B,) or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("seq_lens_k must be [B] and block_table [B, max_blocks]")
+    if q.dtype != torch.bfloat16 or kv_pool.dtype != torch.bfloat16:
+        raise TypeError("paged prefill takes bf16 q and kv_pool")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    if not return_lse:
+        lse = None
+    _check_dev(q, kv_pool, block_table, seq_lens_k, cu_seqlens_q, o, lse)
+    with torch.cuda.device(q.device):
+        _call(lib().fa_prefill_paged(B, H, Hkv, d, int(max_seqlen_q), total, _ptr(cu_seqlens_q), _ptr(q),
+                                     _ptr(kv_pool), page, P, _ptr(block_table), block_table.shape[1],
+                                     _ptr(seq_lens_k), _ptr(o), _ptr(lse), int(bool(causal)), float(scale),
+                                     _stream(q)))
     return o, lse

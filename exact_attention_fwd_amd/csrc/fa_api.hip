@@ -103,7 +103,7 @@ static fa_status forward_impl(fa_dtype dt, fa::AttnShape sh, int d, const void* 
   if (!q || !k || !v || !o) return FA_ERR_NULL_PTR;
   st = device_ready();
   if (st != FA_OK) return st;
-  fa::ForwardArgs a{dt == FA_BF16, sh, d, q, k, v, o, lse, causal != 0, scale, (hipStream_t)stream};
+  fa::ForwardArgs a{dt == FA_BF16, sh, fa::PagedKV{}, d, q, k, v, o, lse, causal != 0, scale, (hipStream_t)stream};
   return hip_status(fa::launch_forward(a));
 }
 
@@ -123,6 +123,27 @@ fa_status fa_forward_varlen(fa_dtype dt, int B, int H, int Hkv, int max_seqlen, 
   if (!cu_seqlens && B > 0) return FA_ERR_NULL_PTR;
   return forward_impl(dt, fa::AttnShape{B, H, Hkv, max_seqlen, total, cu_seqlens}, d, q, k, v, o, lse, causal,
                       scale, stream);
+}
+
+fa_status fa_prefill_paged(int B, int H, int Hkv, int d, int max_seqlen_q, int total_q,
+                           const int32_t* cu_seqlens_q, const void* q, const void* kv_pool, int page_size,
+                           int num_pages, const int32_t* block_table, int max_blocks_per_seq,
+                           const int32_t* seq_lens_k, void* o, float* lse, int causal, float scale, void* stream) {
+  fa_status st = check_common(B, H, Hkv, d, max_seqlen_q, (long long)H * d, scale);
+  if (st != FA_OK) return st;
+  if (total_q < 0 || num_pages <= 0 || max_blocks_per_seq <= 0) return FA_ERR_BAD_SHAPE;
+  if (page_size != 256) return FA_ERR_UNSUPPORTED;
+  if (max_blocks_per_seq > fa::kMaxPrefillPages) return FA_ERR_UNSUPPORTED;
+  if (!fits(num_pages, 2, page_size, (long long)Hkv * d)) return FA_ERR_BAD_SHAPE;
+  if (max_seqlen_q == 0 || total_q == 0) return FA_OK;
+  if (!cu_seqlens_q || !q || !kv_pool || !block_table || !seq_lens_k || !o) return FA_ERR_NULL_PTR;
+  st = device_ready();
+  if (st != FA_OK) return st;
+  fa::ForwardArgs a{true,
+                    fa::AttnShape{B, H, Hkv, max_seqlen_q, total_q, cu_seqlens_q},
+                    fa::PagedKV{kv_pool, block_table, seq_lens_k, max_blocks_per_seq, num_pages},
+                    d, q, nullptr, nullptr, o, lse, causal != 0, scale, (hipStream_t)stream};
+  return hip_status(fa::launch_forward(a));
 }
 
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {

@@ -65,10 +65,12 @@ __device__ __forceinline__ void map_unit(int bid, int B, int H, int& rank, int& 
 // the result is the same exact quantity (only rounding differs).
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int D, bool CAUSAL>
+constexpr int kPage = 256;  // tokens per page of a paged key/value pool
+
+template <int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, AttnShape shape, float scale_log2) {
+    bf16* __restrict__ O, float* __restrict__ LSE, AttnShape shape, PagedKV pkv, float scale_log2) {
   constexpr int KSTEPS = D / 16;  // MFMA k-steps over the head dim
   constexpr int DBLK = D / 32;    // 32-row output blocks over the head dim
   constexpr int TILE = kTileRows * D;
@@ -80,6 +82,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 smem[4 * TILE];
   bf16* const kring = smem;
   bf16* const vring = smem + 2 * TILE;
+  __shared__ int ptab[PAGED ? kMaxPrefillPages : 1];  // this sequence's pool pages
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -88,15 +91,35 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   int rank, bi, hi;
   map_unit(blockIdx.x, shape.B, shape.H, rank, bi, hi);
   const HeadView hv = head_view(shape, bi, hi, D);
-  const int N = hv.L;  // this sequence's length
+  const int N = hv.L;  // this sequence's queries
   const int nqb = (N + kBR - 1) / kBR;
   if (rank >= nqb) return;  // a shorter sequence of a packed batch: no tile of this rank
   const int qb = CAUSAL ? nqb - 1 - rank : rank;  // causal: the last query tiles see the most keys
   const int q0 = qb * kBR;
+  // Keys of this sequence and the causal offset: query q sees keys 0 .. q + off.
+  int Nk = N, off = 0;
+  const int kvs = PAGED ? shape.Hkv * D : hv.kvs;  // elements between consecutive key rows
+  const int hkv = hi / (shape.H / shape.Hkv);
+  if constexpr (PAGED) {
+    Nk = min(max(pkv.seq_lens[bi], 0), pkv.max_blocks * kPage);
+    off = Nk - N;
+    const int np = (Nk + kPage - 1) / kPage;
+    for (int i = tid; i < np; i += kThreads)
+      ptab[i] = min(max(pkv.block_table[(size_t)bi * pkv.max_blocks + i], 0), pkv.num_pages - 1);
+    __syncthreads();
+  }
 
   const auto rq = make_rsrc(Q + hv.q_off, (uint32_t)N * hv.qs * 2);
   const auto rk = make_rsrc(K + hv.kv_off, (uint32_t)N * hv.kvs * 2);
   const auto rv = make_rsrc(V + hv.kv_off, (uint32_t)N * hv.kvs * 2);
+  // Paged: key tile t (64 rows) is rows (t % 4)·64.. of pool page ptab[t / 4]; its
+  // descriptor ends at the sequence's last key, so later slots are never fetched.
+  auto page_rsrc = [&](int t, int half) {
+    const bf16* base = static_cast<const bf16*>(pkv.pool) +
+                       ((size_t)ptab[t >> 2] * 2 * kPage + (size_t)half * kPage + (t & 3) * kTileRows) * kvs +
+                       (size_t)hkv * D;
+    return make_rsrc(base, (uint32_t)min(kTileRows, Nk - t * kTileRows) * kvs * 2);
+  };
   const int qw = q0 + wave * 32;
   const int qrow = qw + n;  // this lane's query
 
@@ -114,18 +137,34 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
   for (int i = 0; i < DMA_PER_WAVE; ++i) {
     const int row = (wave * DMA_PER_WAVE + i) * ROWS_PER_DMA + dma_row;
-    kdma[i] = (uint32_t)row * (hv.kvs * 2) + ((dma_pc ^ rm_swz<D>(row)) << 4);
-    vdma[i] = (uint32_t)row * (hv.kvs * 2) + ((dma_pc ^ v_swz<D>(row)) << 4);
+    kdma[i] = (uint32_t)row * (kvs * 2) + ((dma_pc ^ rm_swz<D>(row)) << 4);
+    vdma[i] = (uint32_t)row * (kvs * 2) + ((dma_pc ^ v_swz<D>(row)) << 4);
   }
   auto issue_k = [&](int t) {
+    if constexpr (PAGED) {
+      const auto r = page_rsrc(t, 0);
 #pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i)
-      lds_dma16(rk, kring + (t & 1) * TILE + (wave * DMA_PER_WAVE + i) * 512, kdma[i] + (uint32_t)t * (64 * hv.kvs * 2));
+      for (int i = 0; i < DMA_PER_WAVE; ++i)
+        lds_dma16(r, kring + (t & 1) * TILE + (wave * DMA_PER_WAVE + i) * 512, kdma[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < DMA_PER_WAVE; ++i)
+        lds_dma16(rk, kring + (t & 1) * TILE + (wave * DMA_PER_WAVE + i) * 512,
+                  kdma[i] + (uint32_t)t * (64 * kvs * 2));
+    }
   };
   auto issue_v = [&](int t) {
+    if constexpr (PAGED) {
+      const auto r = page_rsrc(t, 1);
 #pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i)
-      lds_dma16(rv, vring + (t & 1) * TILE + (wave * DMA_PER_WAVE + i) * 512, vdma[i] + (uint32_t)t * (64 * hv.kvs * 2));
+      for (int i = 0; i < DMA_PER_WAVE; ++i)
+        lds_dma16(r, vring + (t & 1) * TILE + (wave * DMA_PER_WAVE + i) * 512, vdma[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < DMA_PER_WAVE; ++i)
+        lds_dma16(rv, vring + (t & 1) * TILE + (wave * DMA_PER_WAVE + i) * 512,
+                  vdma[i] + (uint32_t)t * (64 * kvs * 2));
+    }
   };
 
   // Per-lane LDS element offsets of the operand reads (loop invariant).
@@ -151,15 +190,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(ks + kb * 32 * D + koff[kk]), qreg[kk], s[kb]);
     }
   };
-  // Future keys (causal diagonal) and keys past N get -inf.
+  // Future keys (causal diagonal) and keys past the sequence's last get -inf.
   auto mask = [&](int k0, f32x16* s) {
-    if ((CAUSAL && k0 + kBC - 1 > qw) || (k0 + kBC > N)) {
+    if ((CAUSAL && k0 + kBC - 1 > qw + off) || (k0 + kBC > Nk)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + crow(kb, r, g);
-          const bool dead = (key >= N) || (CAUSAL && key > qrow);
+          const bool dead = (key >= Nk) || (CAUSAL && key > qrow + off);
           s[kb][r] = dead ? kNegInf : s[kb][r];
         }
     }
@@ -181,14 +220,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   float m_run = kNegInf;  // reference max of s·scale·log2e (lags the true max by < 2^threshold)
   float l_run = 0.f;      // this lane's part of the normaliser
 
-  const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
+  const int kv_end = CAUSAL ? min(Nk, max(q0 + kBR + off, 0)) : Nk;
   const int ntiles = (kv_end + kBC - 1) / kBC;
-  // tiles this wave needs (causal: up to its last query; none past N)
-  const int wnt = (qw >= N) ? 0 : (CAUSAL ? min(ntiles, (min(qw + 31, N - 1) / kBC) + 1) : ntiles);
+  // tiles this wave needs (causal: up to its last query's last key; none past the keys)
+  const int wlast = min(qw + 31, N - 1) + off;  // causal: this wave's last visible key
+  const int wnt = (qw >= N) ? 0 : (CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / kBC + 1)) : ntiles);
 
-  issue_k(0);
+  if (ntiles > 0) issue_k(0);
   if (ntiles > 1) issue_k(1);
-  issue_v(0);
+  if (ntiles > 0) issue_v(0);
   wait_vm_all();
   __syncthreads();
   f32x16 sa[2], sb[2];
@@ -207,8 +247,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     if (t + 2 < ntiles) issue_k(t + 2);
     if (t + 1 < ntiles) issue_v(t + 1);
     bf16* vs = vring + (t & 1) * TILE;
-    if (k0 + kBC > N) {  // tail tile: V rows past N must read as zero, whatever the loads left
-      const int first = N - k0;
+    if (k0 + kBC > Nk) {  // tail tile: V rows past the last key must read as zero, whatever the loads left
+      const int first = Nk - k0;
       for (int idx = tid; idx < (kBC - first) * CPR; idx += kThreads) {
         const u32x4 z = {0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(vs + (first + idx / CPR) * D + (idx % CPR) * 8) = z;
@@ -289,7 +329,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   if (qw >= N || qrow >= N) return;
   const float l_tot = xhalf_sum(l_run);
-  const float inv = 1.f / l_tot;
+  // A query that sees no key (paged causal prefill with fewer keys than queries
+  // before it) has an empty softmax: O = 0, LSE = -inf.
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   bf16* Orow = O + hv.q_off + (size_t)qrow * hv.qs;
 #pragma unroll
   for (int b = 0; b < DBLK; ++b)
@@ -300,7 +342,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       w[1] = pack_bf16x2(oacc[b][4 * i + 2] * inv, oacc[b][4 * i + 3] * inv);
       *reinterpret_cast<u32x2*>(Orow + 32 * b + 8 * i + 4 * g) = w;
     }
-  if (LSE != nullptr && g == 0) LSE[hv.st_off + qrow] = (m_run + log2_fast(l_tot)) * kLn2;
+  if (LSE != nullptr && g == 0) LSE[hv.st_off + qrow] = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : kNegInf;
 }
 
 // fp32 path: one thread per query row, keys staged through LDS 32 at a time,
@@ -363,19 +405,21 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
   if (LSE != nullptr) LSE[hv.st_off + row] = m + logf(l);
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch_bf16(const ForwardArgs& a) {
   const int nqb = (a.s.N + kBR - 1) / kBR;
   const dim3 grid((unsigned)(nqb * a.s.B * a.s.H)), block(kThreads);
   const float sl2 = a.scale * kLog2e;
   auto* q = static_cast<const bf16*>(a.q);
-  auto* k = static_cast<const bf16*>(a.k);
-  auto* v = static_cast<const bf16*>(a.v);
+  auto* k = static_cast<const bf16*>(PAGED ? a.kv.pool : a.k);
+  auto* v = static_cast<const bf16*>(PAGED ? a.kv.pool : a.v);
   auto* o = static_cast<bf16*>(a.o);
   if (a.causal)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.s, sl2);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, true, PAGED>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.s, a.kv,
+                       sl2);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.s, sl2);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, false, PAGED>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.s, a.kv,
+                       sl2);
   return hipGetLastError();
 }
 
@@ -391,7 +435,8 @@ hipError_t launch_f32(const ForwardArgs& a) {
 }  // namespace
 
 hipError_t launch_forward(const ForwardArgs& a) {
-  if (a.bf16) return a.d == 128 ? launch_bf16<128>(a) : launch_bf16<64>(a);
+  if (a.bf16 && a.kv.pool != nullptr) return a.d == 128 ? launch_bf16<128, true>(a) : launch_bf16<64, true>(a);
+  if (a.bf16) return a.d == 128 ? launch_bf16<128, false>(a) : launch_bf16<64, false>(a);
   return a.d == 128 ? launch_f32<128>(a) : launch_f32<64>(a);
 }
 

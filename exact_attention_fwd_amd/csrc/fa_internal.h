@@ -18,9 +18,23 @@ struct AttnShape {
   const int32_t* cu;  // nullptr: dense
 };
 
+// Keys/values read through a page table instead of the query layout: the
+// pool is [num_pages, 2 (K, V), 256, Hkv, d]; sequence b owns seq_lens[b]
+// keys whose logical page p sits at pool page block_table[b·max_blocks + p].
+// Its queries are the last rows of those keys (causal: query i of a sequence
+// with n queries sees keys 0 .. i + seq_lens[b] − n).
+struct PagedKV {
+  const void* pool;  // nullptr: K/V laid out like the queries
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int max_blocks, num_pages;
+};
+constexpr int kMaxPrefillPages = 512;  // block-table entries a paged prefill sequence may use
+
 struct ForwardArgs {
   bool bf16;
   AttnShape s;
+  PagedKV kv;
   int d;
   const void* q;
   const void* k;

@@ -236,6 +236,38 @@ fa_status fa_decode_paged_gqa(int num_seqs, int H, int Hkv, int d, int page_size
                               void* o, float* lse, float scale,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fa_prefill_paged — chunked prefill over a paged KV cache: every sequence
+ * appends a chunk of new tokens to a cached prefix, the chunk's K/V already
+ * written to the pool, and its queries attend through the block table.  The
+ * pool of 256-token pages is the decode one (0539edu.com "Flash不是那个被时代
+ * 淘汰的插件" §2); reusing a cached prefix instead of recomputing it is the
+ * prefix caching of zwxr.cn §5.2.
+ *   cu_seqlens_q  [B+1] int32 (device): sequence b's queries are packed rows
+ *                 cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q.
+ *   max_seqlen_q  largest chunk (host value; sizes the launch).
+ *   q, o          [total_q, H, d] bf16; lse [H, total_q] fp32 or NULL.
+ *   kv_pool       [num_pages, 2, 256, Hkv, d] bf16; query head h reads
+ *                 key/value head h / (H / Hkv).
+ *   block_table   [B, max_blocks_per_seq] int32 (device), max_blocks_per_seq
+ *                 <= 512 (else FA_ERR_UNSUPPORTED).
+ *   seq_lens_k    [B] int32 (device): cached keys of sequence b, prefix plus
+ *                 chunk.  The chunk's queries are the last positions: with
+ *                 causal, query i of a chunk of n sees keys 0 .. i + L_b - n
+ *                 (a query that sees none gets O = 0, LSE = -inf); without,
+ *                 every query sees all L_b keys.
+ * Device-side contents are not validated but never make the kernel touch
+ * memory outside the buffers (table entries are clamped into the pool,
+ * lengths into max_blocks_per_seq·256 and [0, total_q]).  d 64 or 128; bf16
+ * only; other errors as fa_forward.
+ */
+fa_status fa_prefill_paged(int B, int H, int Hkv, int d, int max_seqlen_q, int total_q,
+                           const int32_t* cu_seqlens_q, const void* q,
+                           const void* kv_pool, int page_size, int num_pages,
+                           const int32_t* block_table, int max_blocks_per_seq,
+                           const int32_t* seq_lens_k, void* o, float* lse,
+                           int causal, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,4 +19,5 @@ from .attention import (  # noqa: F401
     attention_backward_gqa,
     attention_forward_varlen,
     attention_backward_varlen,
+    prefill_paged,
 )

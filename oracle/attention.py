@@ -229,6 +229,43 @@ def decode_paged(q, kv_pool, block_table, seq_lens, scale=None, page_size=256):
     return o, lse
 
 
+def prefill_paged(q, kv_pool, block_table, seq_lens_k, cu_seqlens_q, causal=True, scale=None, page_size=256):
+    """Chunked prefill over a paged KV cache.
+
+    Sequence b has L = seq_lens_k[b] cached keys (reached through its block
+    table as in decode_paged) and n = cu[b+1] - cu[b] new queries, packed in
+    q [total_q, H, d].  The queries are the last n positions of the sequence,
+    so with the causal mask query i (0-based in its chunk) sees keys
+    0 .. i + L - n; without it every query sees all L keys.  A query that
+    sees no key has an empty softmax (O = 0, LSE = -inf).  Key/value head of
+    query head h: h // (H // Hkv).  Returns (o [total_q, H, d], lse [H, total_q]).
+    """
+    q, pool = _f64(q), _f64(kv_pool)
+    table = np.asarray(_f64(block_table), dtype=np.int64)
+    lens = np.asarray(_f64(seq_lens_k), dtype=np.int64)
+    cu = np.asarray(_f64(cu_seqlens_q), dtype=np.int64)
+    total, H, d = q.shape
+    Hkv = pool.shape[3]
+    group = H // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.zeros((total, H, d))
+    lse = np.full((H, total), -np.inf)
+    for b in range(len(cu) - 1):
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        n, L = t1 - t0, int(lens[b])
+        if n == 0:
+            continue
+        K, V = gather_pages(pool, table, L, b, page_size)
+        positions = np.arange(n) + (L - n)  # absolute position of each query
+        for h in range(H):
+            s = _mask(_scores(q[t0:t1, h], K[:, h // group], scale), positions, causal)
+            p_, lrow = _softmax_rows(s)
+            o[t0:t1, h] = p_ @ V[:, h // group]
+            lse[h, t0:t1] = lrow
+    return o, lse
+
+
 def online_forward(q, k, v, causal=False, scale=None, tile=16):
     """Tiled single-pass forward with the online softmax (test-only).
 

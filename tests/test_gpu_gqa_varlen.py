@@ -203,3 +203,70 @@ def test_decode_empty_sequence(Hkv):
     keep = [0, 2]
     check("decode empty neighbours O", to64(o)[keep], ro[keep], BF16_MAX, BF16_MEAN)
     check("decode empty neighbours LSE", to64(lse)[keep], rl[keep], LSE_MAX)
+
+
+# ------------------------------------------------------ paged chunked prefill
+def _prefill_compare(name, p, causal):
+    d = p.q.shape[-1]
+    qd, pool, bt, sl, cu = cuda(p.q, p.kv_pool, p.block_table, p.seq_lens_k, p.cu_seqlens_q)
+    mx = int((p.cu_seqlens_q[1:] - p.cu_seqlens_q[:-1]).max())
+    o, lse = fa().prefill_paged(qd, pool, bt, sl, cu, mx, causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill_paged(p.q, p.kv_pool, p.block_table, p.seq_lens_k, p.cu_seqlens_q, causal=causal,
+                                  scale=1 / math.sqrt(d), page_size=p.page_size)
+    o64, l64 = to64(o), to64(lse)
+    empty = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(l64), empty), "rows that see no key must give LSE = -inf"
+    check(f"{name} O", o64, ro, BF16_MAX, BF16_MEAN)
+    check(f"{name} LSE", l64[~empty], rl[~empty], LSE_MAX)
+    return o, lse
+
+
+PREFILL = {
+    # chunk lengths, cached keys (prefix + chunk)
+    "prefix": ([300, 1, 64, 257, 513], [1000, 513, 64, 300, 2048]),
+    "no_prefix": ([200, 77, 256], [200, 77, 256]),
+    "decode_like": ([1, 1, 1], [1, 255, 4097]),
+}
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("case", sorted(PREFILL))
+def test_prefill_paged(case, causal, d):
+    chunks, ctx = PREFILL[case]
+    print(f"[prefill] {case} causal={causal} d={d}", flush=True)
+    p = workloads.prefill_inputs(chunks, ctx, H=8, Hkv=2, d=d, seed=len(chunks) + d, poison=True, spare_pages=3)
+    _prefill_compare(f"prefill {case}", p, causal)
+
+
+@pytest.mark.parametrize("Hkv", [8, 1])
+def test_prefill_paged_heads(Hkv):
+    p = workloads.prefill_inputs([130, 40], [900, 40], H=8, Hkv=Hkv, d=128, seed=Hkv)
+    _prefill_compare(f"prefill Hkv={Hkv}", p, True)
+
+
+def test_prefill_more_queries_than_keys():
+    """Causal rows before the first cached key are empty: O = 0, LSE = -inf."""
+    p = workloads.prefill_inputs([70, 5], [40, 5], H=4, Hkv=4, d=64, seed=3)
+    o, lse = _prefill_compare("prefill n > L", p, True)
+    assert (o[:30] == 0).all() and torch.isneginf(lse[:, :30]).all()
+
+
+def test_prefill_without_prefix_matches_varlen_forward():
+    """With no cached prefix the paged prefill is the packed causal forward."""
+    p = workloads.prefill_inputs([333, 64], [333, 64], H=4, Hkv=4, d=128, seed=17)
+    qd, pool, bt, sl, cu = cuda(p.q, p.kv_pool, p.block_table, p.seq_lens_k, p.cu_seqlens_q)
+    o, lse = fa().prefill_paged(qd, pool, bt, sl, cu, 333, causal=True)
+    # the same keys/values gathered into the packed layout
+    pool_c = p.kv_pool
+    ks, vs = [], []
+    for b, L in enumerate(p.seq_lens_k.tolist()):
+        for t in range(L):
+            pg = int(p.block_table[b, t // 256])
+            ks.append(pool_c[pg, 0, t % 256])
+            vs.append(pool_c[pg, 1, t % 256])
+    k, v = torch.stack(ks).to(DEV), torch.stack(vs).to(DEV)
+    o2, lse2 = fa().forward_varlen(qd, k, v, cu, 333, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)

@@ -178,3 +178,34 @@ def varlen_inputs(lens, H, Hkv, d, dtype="bf16", seed=0, with_dout=False):
     if not with_dout:
         return cu, q, k, v
     return cu, q, k, v, _draw(g, (total, H, d), dtype)
+
+
+@dataclass
+class PrefillInputs:
+    q: torch.Tensor            # [total_q, H, d] bf16, the new chunk of every sequence, packed
+    cu_seqlens_q: torch.Tensor # [B+1] int32
+    kv_pool: torch.Tensor      # [P, 2, page, Hkv, d] bf16 (each sequence's prefix and chunk)
+    block_table: torch.Tensor  # [B, max_blocks] int32, -1 past the last page
+    seq_lens_k: torch.Tensor   # [B] int32, cached keys per sequence (prefix + chunk)
+    page_size: int
+
+
+def prefill_inputs(chunk_lens, ctx_lens, H=32, Hkv=None, d=128, max_blocks=None, seed=0,
+                   page_size=PAGE_SIZE, poison=False, spare_pages=0):
+    """A chunked prefill over a paged cache: sequence b has ctx_lens[b] cached
+    keys (its prefix followed by its new chunk) and chunk_lens[b] new queries.
+    The pool is drawn exactly as paged_inputs() draws a decode cache (same
+    seed, lengths ctx_lens); the packed queries are drawn afterwards from a
+    second generator seeded seed + 1."""
+    chunk_lens = [int(x) for x in chunk_lens]
+    ctx_lens = [int(x) for x in ctx_lens]
+    B = len(ctx_lens)
+    pages = [max(1, (L + page_size - 1) // page_size) for L in ctx_lens]
+    mb = max(pages) if max_blocks is None else max_blocks
+    p = paged_inputs(num_seqs=B, H=H, d=d, max_blocks=mb, seed=seed, page_size=page_size, poison=poison,
+                     spare_pages=spare_pages, seq_lens=[max(L, 1) for L in ctx_lens], Hkv=Hkv)
+    g = _gen(seed + 1)
+    import itertools
+    cu = torch.tensor([0] + list(itertools.accumulate(chunk_lens)), dtype=torch.int32)
+    q = _draw(g, (int(cu[-1]), H, d), "bf16")
+    return PrefillInputs(q, cu, p.kv_pool, p.block_table, torch.tensor(ctx_lens, dtype=torch.int32), page_size)
