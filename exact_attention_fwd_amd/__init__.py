@@ -34,6 +34,7 @@ __all__ = [
     "backward_varlen",
     "decode_paged",
     "prefill_paged",
+    "forward_rope",
     "backward_workspace_bytes",
     "decode_workspace_bytes",
     "FaError",
@@ -254,13 +255,72 @@ def decode_paged(q, kv_pool, block_table, seq_lens, scale: float | None = None, 
     return o, lse
 
 
+def _rope_args(rope_cos, rope_sin, d):
+    torch = _torch()
+    if rope_cos is None and rope_sin is None:
+        return None, None, 0
+    if rope_cos is None or rope_sin is None:
+        raise ValueError("pass both rotary tables or neither")
+    for t in (rope_cos, rope_sin):
+        if t.dtype != torch.float32 or t.dim() != 2 or t.shape[1] != d // 2:
+            raise ValueError("rotary tables must be fp32 [rows, d/2]")
+    if rope_cos.shape != rope_sin.shape:
+        raise ValueError("rotary tables must have the same shape")
+    return rope_cos, rope_sin, rope_cos.shape[0]
+
+
+def forward_rope(q, k, v, rope_cos, rope_sin, causal: bool = False, scale: float | None = None,
+                 interleaved: bool = False, cu_seqlens=None, max_seqlen: int | None = None, out=None, lse=None,
+                 return_lse: bool = True):
+    """Forward with the rotary embedding of Q and K fused into the kernel.
+    Dense: q [B, H, N, d], k/v [B, Hkv, N, d]; packed (cu_seqlens given):
+    q [total, H, d], k/v [total, Hkv, d].  rope_cos / rope_sin fp32
+    [rows, d/2] with rows >= N (max_seqlen): position p rotates feature pair
+    i (i, i + d/2), or (2i, 2i+1) when interleaved, by cos[p][i], sin[p][i].
+    Returns (o, lse) laid out as forward / forward_varlen."""
+    torch = _torch()
+    packed = cu_seqlens is not None
+    if packed:
+        total, H, d = q.shape
+        Hkv = k.shape[1]
+        B = cu_seqlens.numel() - 1
+        N = int(max_seqlen)
+        lse_shape = (H, total)
+    else:
+        B, H, N, d = q.shape
+        Hkv = k.shape[1]
+        total = 0
+        lse_shape = (B, H, N)
+    if v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must match and share q's dtype")
+    cos_t, sin_t, rows = _rope_args(rope_cos, rope_sin, d)
+    if cos_t is None:
+        raise ValueError("forward_rope needs the rotary tables")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    if not return_lse:
+        lse = None
+    _check_dev(q, k, v, cos_t, sin_t, o, lse, *( [cu_seqlens] if packed else [] ))
+    with torch.cuda.device(q.device):
+        _call(lib().fa_forward_rope(_dtype_code(q), B, H, Hkv, N, total, d, _ptr(cu_seqlens), _ptr(q), _ptr(k),
+                                    _ptr(v), _ptr(o), _ptr(lse), int(bool(causal)), float(scale), _ptr(cos_t),
+                                    _ptr(sin_t), rows, int(bool(interleaved)), _stream(q)))
+    return o, lse
+
+
 def prefill_paged(q, kv_pool, block_table, seq_lens_k, cu_seqlens_q, max_seqlen_q: int, causal: bool = True,
-                  scale: float | None = None, out=None, lse=None, return_lse: bool = True):
+                  scale: float | None = None, out=None, lse=None, return_lse: bool = True, rope_cos=None,
+                  rope_sin=None, rope_interleaved: bool = False):
     """Chunked prefill over a paged KV cache: q [total_q, H, d] bf16 (the new
     chunk of every sequence, packed by cu_seqlens_q int32 [B+1]); kv_pool
     [P, 2, page, Hkv, d] bf16 holding each sequence's seq_lens_k[b] keys
     (prefix, then the chunk) through block_table [B, max_blocks] int32.
     Causal: query i of a chunk of n sees keys 0 .. i + seq_lens_k[b] - n.
+    With rotary tables the queries are rotated at those positions (the cached
+    keys are taken as stored, already rotated).
     Returns (o [total_q, H, d] bf16, lse [H, total_q] fp32 or None)."""
     torch = _torch()
     if q.dim() != 3 or kv_pool.dim() != 5 or kv_pool.shape[1] != 2 or kv_pool.shape[4] != q.shape[2]:
@@ -283,10 +343,11 @@ def prefill_paged(q, kv_pool, block_table, seq_lens_k, cu_seqlens_q, max_seqlen_
         lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
     if not return_lse:
         lse = None
-    _check_dev(q, kv_pool, block_table, seq_lens_k, cu_seqlens_q, o, lse)
+    cos_t, sin_t, rows = _rope_args(rope_cos, rope_sin, d)
+    _check_dev(q, kv_pool, block_table, seq_lens_k, cu_seqlens_q, o, lse, cos_t, sin_t)
     with torch.cuda.device(q.device):
         _call(lib().fa_prefill_paged(B, H, Hkv, d, int(max_seqlen_q), total, _ptr(cu_seqlens_q), _ptr(q),
                                      _ptr(kv_pool), page, P, _ptr(block_table), block_table.shape[1],
                                      _ptr(seq_lens_k), _ptr(o), _ptr(lse), int(bool(causal)), float(scale),
-                                     _stream(q)))
+                                     _ptr(cos_t), _ptr(sin_t), rows, int(bool(rope_interleaved)), _stream(q)))
     return o, lse

@@ -83,8 +83,11 @@ def _declare(L):
                                       c_float, vp, c_size, vp]
     L.fa_decode_paged_gqa.restype = c_int
     L.fa_prefill_paged.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, vp, vp, vp, c_int, c_int, vp, c_int,
-                                   vp, vp, vp, c_int, c_float, vp]
+                                   vp, vp, vp, c_int, c_float, vp, vp, c_int, c_int, vp]
     L.fa_prefill_paged.restype = c_int
+    L.fa_forward_rope.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp, c_int,
+                                  c_float, vp, vp, c_int, c_int, vp]
+    L.fa_forward_rope.restype = c_int
 
 
 def lib():

@@ -91,7 +91,8 @@ static fa_status check_common(int B, int H, int Hkv, int d, long long rows_max, 
 }
 
 static fa_status forward_impl(fa_dtype dt, fa::AttnShape sh, int d, const void* q, const void* k, const void* v,
-                              void* o, float* lse, int causal, float scale, void* stream) {
+                              void* o, float* lse, int causal, float scale, void* stream,
+                              fa::RopeArgs rope = fa::RopeArgs{}) {
   if (dt != FA_F32 && dt != FA_BF16) return FA_ERR_UNSUPPORTED;
   const bool packed = sh.cu != nullptr;
   fa_status st = check_common(sh.B, sh.H, sh.Hkv, d, sh.N, packed ? (long long)sh.H * d : d, scale);
@@ -103,7 +104,8 @@ static fa_status forward_impl(fa_dtype dt, fa::AttnShape sh, int d, const void* 
   if (!q || !k || !v || !o) return FA_ERR_NULL_PTR;
   st = device_ready();
   if (st != FA_OK) return st;
-  fa::ForwardArgs a{dt == FA_BF16, sh, fa::PagedKV{}, d, q, k, v, o, lse, causal != 0, scale, (hipStream_t)stream};
+  fa::ForwardArgs a{dt == FA_BF16, sh, fa::PagedKV{}, rope, d, q, k, v, o, lse, causal != 0, scale,
+                    (hipStream_t)stream};
   return hip_status(fa::launch_forward(a));
 }
 
@@ -125,12 +127,44 @@ fa_status fa_forward_varlen(fa_dtype dt, int B, int H, int Hkv, int max_seqlen, 
                       scale, stream);
 }
 
+// Rotary tables: both or neither, 16-byte aligned, at least one row.
+static fa_status check_rope(const float* cos_t, const float* sin_t, int rows, fa::RopeArgs& out) {
+  out = fa::RopeArgs{};
+  if (!cos_t && !sin_t) return FA_OK;
+  if (!cos_t || !sin_t) return FA_ERR_NULL_PTR;
+  if (rows <= 0 || (reinterpret_cast<uintptr_t>(cos_t) & 15) || (reinterpret_cast<uintptr_t>(sin_t) & 15))
+    return FA_ERR_BAD_SHAPE;
+  out = fa::RopeArgs{cos_t, sin_t, rows, 0};
+  return FA_OK;
+}
+
+fa_status fa_forward_rope(fa_dtype dt, int B, int H, int Hkv, int N, int total, int d, const int32_t* cu_seqlens,
+                          const void* q, const void* k, const void* v, void* o, float* lse, int causal, float scale,
+                          const float* rope_cos, const float* rope_sin, int rope_rows, int rope_interleaved,
+                          void* stream) {
+  if (dt != FA_BF16) return FA_ERR_UNSUPPORTED;
+  fa::RopeArgs rope;
+  fa_status st = check_rope(rope_cos, rope_sin, rope_rows, rope);
+  if (st != FA_OK) return st;
+  if (!rope.cos) return FA_ERR_NULL_PTR;
+  if (rope_rows < N) return FA_ERR_BAD_SHAPE;  // every position 0 .. N-1 needs a row
+  rope.interleaved = rope_interleaved != 0;
+  return forward_impl(dt, fa::AttnShape{B, H, Hkv, N, cu_seqlens ? total : 0, cu_seqlens}, d, q, k, v, o, lse,
+                      causal, scale, stream, rope);
+}
+
 fa_status fa_prefill_paged(int B, int H, int Hkv, int d, int max_seqlen_q, int total_q,
                            const int32_t* cu_seqlens_q, const void* q, const void* kv_pool, int page_size,
                            int num_pages, const int32_t* block_table, int max_blocks_per_seq,
-                           const int32_t* seq_lens_k, void* o, float* lse, int causal, float scale, void* stream) {
+                           const int32_t* seq_lens_k, void* o, float* lse, int causal, float scale,
+                           const float* rope_cos, const float* rope_sin, int rope_rows, int rope_interleaved,
+                           void* stream) {
   fa_status st = check_common(B, H, Hkv, d, max_seqlen_q, (long long)H * d, scale);
   if (st != FA_OK) return st;
+  fa::RopeArgs rope;
+  st = check_rope(rope_cos, rope_sin, rope_rows, rope);
+  if (st != FA_OK) return st;
+  rope.interleaved = rope_interleaved != 0;
   if (total_q < 0 || num_pages <= 0 || max_blocks_per_seq <= 0) return FA_ERR_BAD_SHAPE;
   if (page_size != 256) return FA_ERR_UNSUPPORTED;
   if (max_blocks_per_seq > fa::kMaxPrefillPages) return FA_ERR_UNSUPPORTED;
@@ -142,7 +176,7 @@ fa_status fa_prefill_paged(int B, int H, int Hkv, int d, int max_seqlen_q, int t
   fa::ForwardArgs a{true,
                     fa::AttnShape{B, H, Hkv, max_seqlen_q, total_q, cu_seqlens_q},
                     fa::PagedKV{kv_pool, block_table, seq_lens_k, max_blocks_per_seq, num_pages},
-                    d, q, nullptr, nullptr, o, lse, causal != 0, scale, (hipStream_t)stream};
+                    rope, d, q, nullptr, nullptr, o, lse, causal != 0, scale, (hipStream_t)stream};
   return hip_status(fa::launch_forward(a));
 }
 

@@ -67,10 +67,51 @@ constexpr float kRescaleThreshold = 8.0f;
 
 constexpr int kPage = 256;  // tokens per page of a paged key/value pool
 
-template <int D, bool CAUSAL, bool PAGED>
+// Rotate the feature pairs (x[j], y[j]) of 8 bf16 values each by the angles
+// whose cosines / sines are c[j], s[j]; bf16 (RNE) results.  Each product is
+// rounded to fp32 on its own (no fused multiply-add), so the value that is
+// rounded to bf16 is fl(fl(x·c) − fl(y·s)), fl(fl(x·s) + fl(y·c)) exactly.
+__device__ __forceinline__ void rotate8(bf16x8& x, bf16x8& y, const float* c, const float* s) {
+#pragma clang fp contract(off)
+  float xr[8], yr[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float a = (float)x[j], b = (float)y[j];
+    xr[j] = a * c[j] - b * s[j];
+    yr[j] = a * s[j] + b * c[j];
+  }
+  x = pack8(xr);
+  y = pack8(yr);
+}
+// Same for the interleaved pairing: pairs (x[2j], x[2j+1]), angles c[j], s[j].
+__device__ __forceinline__ void rotate8_interleaved(bf16x8& x, const float* c, const float* s) {
+#pragma clang fp contract(off)
+  float r[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = (float)x[2 * j], b = (float)x[2 * j + 1];
+    r[2 * j] = a * c[j] - b * s[j];
+    r[2 * j + 1] = a * s[j] + b * c[j];
+  }
+  x = pack8(r);
+}
+template <int N>
+__device__ __forceinline__ void load_f32(float* dst, const float* src) {
+#pragma unroll
+  for (int j = 0; j < N; j += 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + j);
+    dst[j] = v[0];
+    dst[j + 1] = v[1];
+    dst[j + 2] = v[2];
+    dst[j + 3] = v[3];
+  }
+}
+
+template <int D, bool CAUSAL, bool PAGED, bool ROPE>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, AttnShape shape, PagedKV pkv, float scale_log2) {
+    bf16* __restrict__ O, float* __restrict__ LSE, AttnShape shape, PagedKV pkv, RopeArgs rope,
+    float scale_log2) {
   constexpr int KSTEPS = D / 16;  // MFMA k-steps over the head dim
   constexpr int DBLK = D / 32;    // 32-row output blocks over the head dim
   constexpr int TILE = kTileRows * D;
@@ -128,6 +169,66 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk)
     qreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)qrow * (hv.qs * 2) + (16 * kk + 8 * g) * 2));
+
+  // Rotary embedding of this lane's query (position qrow + off; rows past N
+  // take any valid table row: their outputs are never written).
+  if constexpr (ROPE) {
+    const int pos = min(max(qrow + off, 0), rope.rows - 1);
+    const float* cr = rope.cos + (size_t)pos * (D / 2);
+    const float* sr = rope.sin + (size_t)pos * (D / 2);
+    if (!rope.interleaved) {
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS / 2; ++kk) {  // features 16kk+8g.. pair with the same + D/2 (chunk kk + KSTEPS/2)
+        float c[8], sn[8];
+        load_f32<8>(c, cr + 16 * kk + 8 * g);
+        load_f32<8>(sn, sr + 16 * kk + 8 * g);
+        rotate8(qreg[kk], qreg[kk + KSTEPS / 2], c, sn);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {  // pairs (2i, 2i+1) inside the chunk, i from 8kk + 4g
+        float c[4], sn[4];
+        load_f32<4>(c, cr + 8 * kk + 4 * g);
+        load_f32<4>(sn, sr + 8 * kk + 4 * g);
+        rotate8_interleaved(qreg[kk], c, sn);
+      }
+    }
+  }
+  // Rotary embedding of a resident K tile (rows k0.., positions k0 + r), in
+  // place in LDS: once per workgroup and tile, every thread one item.
+  auto rope_k = [&](bf16* ks, int k0) {
+    if constexpr (ROPE && !PAGED) {
+      if (!rope.interleaved) {
+        constexpr int PAIRS = CPR / 2;  // chunk c pairs with chunk c + CPR/2
+        for (int w = tid; w < kTileRows * PAIRS; w += kThreads) {
+          const int r = w / PAIRS, c = w % PAIRS;
+          const int pos = min(k0 + r, rope.rows - 1);
+          bf16x8* px = reinterpret_cast<bf16x8*>(ks + r * D + ((c ^ rm_swz<D>(r)) << 3));
+          bf16x8* py = reinterpret_cast<bf16x8*>(ks + r * D + (((c + PAIRS) ^ rm_swz<D>(r)) << 3));
+          float cs[8], sn[8];
+          load_f32<8>(cs, rope.cos + (size_t)pos * (D / 2) + 8 * c);
+          load_f32<8>(sn, rope.sin + (size_t)pos * (D / 2) + 8 * c);
+          bf16x8 x = *px, y = *py;
+          rotate8(x, y, cs, sn);
+          *px = x;
+          *py = y;
+        }
+      } else {
+        for (int w = tid; w < kTileRows * CPR; w += kThreads) {
+          const int r = w / CPR, c = w % CPR;
+          const int pos = min(k0 + r, rope.rows - 1);
+          bf16x8* px = reinterpret_cast<bf16x8*>(ks + r * D + ((c ^ rm_swz<D>(r)) << 3));
+          float cs[4], sn[4];
+          load_f32<4>(cs, rope.cos + (size_t)pos * (D / 2) + 4 * c);
+          load_f32<4>(sn, rope.sin + (size_t)pos * (D / 2) + 4 * c);
+          bf16x8 x = *px;
+          rotate8_interleaved(x, cs, sn);
+          *px = x;
+        }
+      }
+      __syncthreads();
+    }
+  };
 
   // Direct-to-LDS loads: wave w fills 1 KiB blocks w*DMA_PER_WAVE.. of a tile;
   // lane l writes physical chunk l % CPR of row l / CPR of its block, fetching
@@ -231,6 +332,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   if (ntiles > 0) issue_v(0);
   wait_vm_all();
   __syncthreads();
+  if (ntiles > 0) rope_k(kring, 0);
   f32x16 sa[2], sb[2];
   if (wnt > 0) {
     scores(kring, sa);
@@ -255,6 +357,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       }
       __syncthreads();
     }
+    if (t + 1 < ntiles) rope_k(kring + ((t + 1) & 1) * TILE, (t + 1) * kBC);
     if (t >= wnt) return;
 
     // On a wave's last tile this product reads a stale K tile and is dropped.
@@ -405,7 +508,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
   if (LSE != nullptr) LSE[hv.st_off + row] = m + logf(l);
 }
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool ROPE>
 hipError_t launch_bf16(const ForwardArgs& a) {
   const int nqb = (a.s.N + kBR - 1) / kBR;
   const dim3 grid((unsigned)(nqb * a.s.B * a.s.H)), block(kThreads);
@@ -415,12 +518,19 @@ hipError_t launch_bf16(const ForwardArgs& a) {
   auto* v = static_cast<const bf16*>(PAGED ? a.kv.pool : a.v);
   auto* o = static_cast<bf16*>(a.o);
   if (a.causal)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, true, PAGED>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.s, a.kv,
-                       sl2);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, true, PAGED, ROPE>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.s,
+                       a.kv, a.rope, sl2);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, false, PAGED>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.s, a.kv,
-                       sl2);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, false, PAGED, ROPE>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.s,
+                       a.kv, a.rope, sl2);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bf16_any(const ForwardArgs& a) {
+  const bool paged = a.kv.pool != nullptr, rope = a.rope.cos != nullptr;
+  if (paged) return rope ? launch_bf16<D, true, true>(a) : launch_bf16<D, true, false>(a);
+  return rope ? launch_bf16<D, false, true>(a) : launch_bf16<D, false, false>(a);
 }
 
 template <int D>
@@ -435,8 +545,7 @@ hipError_t launch_f32(const ForwardArgs& a) {
 }  // namespace
 
 hipError_t launch_forward(const ForwardArgs& a) {
-  if (a.bf16 && a.kv.pool != nullptr) return a.d == 128 ? launch_bf16<128, true>(a) : launch_bf16<64, true>(a);
-  if (a.bf16) return a.d == 128 ? launch_bf16<128, false>(a) : launch_bf16<64, false>(a);
+  if (a.bf16) return a.d == 128 ? launch_bf16_any<128>(a) : launch_bf16_any<64>(a);
   return a.d == 128 ? launch_f32<128>(a) : launch_f32<64>(a);
 }
 

@@ -31,10 +31,23 @@ struct PagedKV {
 };
 constexpr int kMaxPrefillPages = 512;  // block-table entries a paged prefill sequence may use
 
+// Rotary position embedding applied inside the forward: the feature pair
+// (x, y) of a row at position p becomes (x·c − y·s, x·s + y·c) with
+// c = cos[p][i], s = sin[p][i] (fp32 tables [rows, d/2]).  Pair i is
+// (i, i + d/2) (half split) or (2i, 2i+1) (interleaved).  Positions are the
+// row's index in its sequence (queries of a paged prefill: i + L − n).
+struct RopeArgs {
+  const float* cos;  // nullptr: no rotation
+  const float* sin;
+  int rows;
+  int interleaved;
+};
+
 struct ForwardArgs {
   bool bf16;
   AttnShape s;
   PagedKV kv;
+  RopeArgs rope;
   int d;
   const void* q;
   const void* k;

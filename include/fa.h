@@ -266,7 +266,36 @@ fa_status fa_prefill_paged(int B, int H, int Hkv, int d, int max_seqlen_q, int t
                            const void* kv_pool, int page_size, int num_pages,
                            const int32_t* block_table, int max_blocks_per_seq,
                            const int32_t* seq_lens_k, void* o, float* lse,
-                           int causal, float scale, void* stream);
+                           int causal, float scale,
+                           const float* rope_cos, const float* rope_sin,
+                           int rope_rows, int rope_interleaved, void* stream);
+
+/*
+ * fa_forward_rope — the forward with the rotary position embedding applied
+ * to Q and K inside the kernel, from precomputed cosine / sine tables (the
+ * fused RoPE with a lookup table of 0539edu.com "Flash不是那个被时代淘汰的
+ * 插件" §3; the rotated Q/K are never written to memory).
+ *   cu_seqlens  NULL: dense, q/o [B, H, N, d] and k/v [B, Hkv, N, d];
+ *               else packed as fa_forward_varlen (N = max_seqlen, total rows).
+ *   rope_cos, rope_sin  fp32 [rope_rows, d/2], 16-byte aligned; rope_rows
+ *               >= N.  A row at position p (its index in its sequence) has
+ *               feature pair i rotated by the angle whose cosine / sine are
+ *               rope_cos[p][i], rope_sin[p][i]:
+ *               (x, y) -> (x·cos − y·sin, x·sin + y·cos).
+ *   rope_interleaved  0: pair i = features (i, i + d/2); 1: (2i, 2i+1).
+ * The rotation runs in fp32 on the bf16 inputs and is rounded to bf16 (RNE)
+ * before the products.  bf16 only.  Other arguments and errors as
+ * fa_forward_gqa / fa_forward_varlen.
+ *
+ * fa_prefill_paged takes the same four rotary arguments (NULL tables: none)
+ * and rotates its queries only, at positions i + L_b − n: the cached keys are
+ * expected to be stored already rotated.
+ */
+fa_status fa_forward_rope(fa_dtype dt, int B, int H, int Hkv, int N, int total, int d,
+                          const int32_t* cu_seqlens, const void* q, const void* k,
+                          const void* v, void* o, float* lse, int causal, float scale,
+                          const float* rope_cos, const float* rope_sin, int rope_rows,
+                          int rope_interleaved, void* stream);
 
 #ifdef __cplusplus
 }

@@ -20,4 +20,7 @@ from .attention import (  # noqa: F401
     attention_forward_varlen,
     attention_backward_varlen,
     prefill_paged,
+    apply_rope,
+    apply_rope_bf16,
+    attention_forward_rope,
 )

@@ -29,6 +29,11 @@ What is computed, and where the pages define it:
   the explainer's 使用门槛和条件 §4: sequences concatenated token-major
   ([total, H, d]), sequence b owning rows cu[b]..cu[b+1]-1, attention (and
   the causal mask) kept inside each sequence, LSE laid out [H, total].
+* Rotary position embedding fused into the forward — the RoPE-with-a-lookup-
+  table fusion of 0539edu.com §3: Q and K rows rotated pairwise by angles
+  read from cosine / sine tables at each row's position before the scores
+  (apply_rope, exact; apply_rope_bf16, the same rotation stored as the bf16
+  operands of the products).
 * online_forward — the tiled online-softmax recurrence of the explainer's
   关键术语解析 §4 (在线 Softmax: the running max and normaliser update), with
   the partial output rescaled alongside the normaliser and divided by the
@@ -229,7 +234,8 @@ def decode_paged(q, kv_pool, block_table, seq_lens, scale=None, page_size=256):
     return o, lse
 
 
-def prefill_paged(q, kv_pool, block_table, seq_lens_k, cu_seqlens_q, causal=True, scale=None, page_size=256):
+def prefill_paged(q, kv_pool, block_table, seq_lens_k, cu_seqlens_q, causal=True, scale=None, page_size=256,
+                  rope=None):
     """Chunked prefill over a paged KV cache.
 
     Sequence b has L = seq_lens_k[b] cached keys (reached through its block
@@ -238,7 +244,10 @@ def prefill_paged(q, kv_pool, block_table, seq_lens_k, cu_seqlens_q, causal=True
     so with the causal mask query i (0-based in its chunk) sees keys
     0 .. i + L - n; without it every query sees all L keys.  A query that
     sees no key has an empty softmax (O = 0, LSE = -inf).  Key/value head of
-    query head h: h // (H // Hkv).  Returns (o [total_q, H, d], lse [H, total_q]).
+    query head h: h // (H // Hkv).  rope = (cos, sin, interleaved) rotates the
+    queries at their positions as apply_rope_bf16 does (the cached keys are
+    used as stored).
+    Returns (o [total_q, H, d], lse [H, total_q]).
     """
     q, pool = _f64(q), _f64(kv_pool)
     table = np.asarray(_f64(block_table), dtype=np.int64)
@@ -258,12 +267,97 @@ def prefill_paged(q, kv_pool, block_table, seq_lens_k, cu_seqlens_q, causal=True
             continue
         K, V = gather_pages(pool, table, L, b, page_size)
         positions = np.arange(n) + (L - n)  # absolute position of each query
+        qb = q[t0:t1]
+        if rope is not None:
+            qb = np.swapaxes(apply_rope_bf16(np.swapaxes(qb, 0, 1), np.maximum(positions, 0), *rope), 0, 1)
         for h in range(H):
-            s = _mask(_scores(q[t0:t1, h], K[:, h // group], scale), positions, causal)
+            s = _mask(_scores(qb[:, h], K[:, h // group], scale), positions, causal)
             p_, lrow = _softmax_rows(s)
             o[t0:t1, h] = p_ @ V[:, h // group]
             lse[h, t0:t1] = lrow
     return o, lse
+
+
+def apply_rope(x, positions, cos, sin, interleaved=False):
+    """Rotary position embedding of rows x [..., n, d] at positions [n], exact.
+
+    Feature pair i of the row at position p is (x_i, x_{i+d/2}) (half split)
+    or (x_{2i}, x_{2i+1}) (interleaved); it becomes
+    (x·cos[p][i] − y·sin[p][i], x·sin[p][i] + y·cos[p][i]).  The tables are
+    inputs (a precomputed lookup, "Flash不是那个被时代淘汰的插件" §3); every
+    value is used in fp64.
+    """
+    x = _f64(x).copy()
+    c = _f64(cos)[np.asarray(positions)]  # [n, d/2]
+    s = _f64(sin)[np.asarray(positions)]
+    d = x.shape[-1]
+    if interleaved:
+        a, b = x[..., 0::2].copy(), x[..., 1::2].copy()
+        x[..., 0::2] = a * c - b * s
+        x[..., 1::2] = a * s + b * c
+    else:
+        a, b = x[..., : d // 2].copy(), x[..., d // 2:].copy()
+        x[..., : d // 2] = a * c - b * s
+        x[..., d // 2:] = a * s + b * c
+    return x
+
+
+def _bf16_rne(x32: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16, to nearest with ties to even (finite inputs):
+    add 0x7FFF plus the lowest kept bit to the raw fp32 bits, clear the low
+    16 bits."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def apply_rope_bf16(x, positions, cos, sin, interleaved=False):
+    """The rotation as it is stored for bf16 matrix products.
+
+    The attention products take bf16 operands, so the rotated rows are rounded
+    to bf16 (round-to-nearest-even) — a quantisation of each rotated feature.
+    Both sides take that rounding from the same fp32 value: each feature is
+    computed from the stored bf16 input and the fp32 table entries with IEEE
+    fp32 operations, each product rounded on its own (no fused multiply-add):
+    fl(fl(x·c) − fl(y·s)) and fl(fl(x·s) + fl(y·c)).  Returns fp64 arrays
+    holding those bf16 values; apply_rope is the exact rotation they round.
+    """
+    x32 = _f64(x).astype(np.float32)
+    pos = np.asarray(positions)
+    c = _f64(cos).astype(np.float32)[pos]
+    s = _f64(sin).astype(np.float32)[pos]
+    d = x32.shape[-1]
+    if interleaved:
+        a, b = x32[..., 0::2], x32[..., 1::2]
+    else:
+        a, b = x32[..., : d // 2], x32[..., d // 2:]
+    first = np.float32(a * c) - np.float32(b * s)
+    second = np.float32(a * s) + np.float32(b * c)
+    out = np.empty(x32.shape, dtype=np.float64)
+    if interleaved:
+        out[..., 0::2], out[..., 1::2] = _bf16_rne(first), _bf16_rne(second)
+    else:
+        out[..., : d // 2], out[..., d // 2:] = _bf16_rne(first), _bf16_rne(second)
+    return out
+
+
+def attention_forward_rope(q, k, v, cos, sin, causal=False, scale=None, interleaved=False, cu_seqlens=None,
+                           rotate=apply_rope_bf16):
+    """Forward with Q and K rotated first (by default the bf16-stored
+    rotation, apply_rope_bf16; pass rotate=apply_rope for the exact one).
+    Dense: q [B, H, N, d], k/v [B, Hkv, N, d], positions 0..N-1.  Packed
+    (cu_seqlens): [total, heads, d], positions counted from each sequence's
+    first row."""
+    if cu_seqlens is None:
+        N = q.shape[2]
+        pos = np.arange(N)
+        return attention_forward_gqa(rotate(q, pos, cos, sin, interleaved),
+                                     rotate(k, pos, cos, sin, interleaved), v, causal=causal, scale=scale)
+    cu = np.asarray(_f64(cu_seqlens), dtype=np.int64)
+    pos = np.concatenate([np.arange(cu[b + 1] - cu[b]) for b in range(len(cu) - 1)]).astype(np.int64)
+    qr = np.swapaxes(rotate(np.swapaxes(_f64(q), 0, 1), pos, cos, sin, interleaved), 0, 1)
+    kr = np.swapaxes(rotate(np.swapaxes(_f64(k), 0, 1), pos, cos, sin, interleaved), 0, 1)
+    return attention_forward_varlen(qr, kr, v, cu_seqlens, causal=causal, scale=scale)
 
 
 def online_forward(q, k, v, causal=False, scale=None, tile=16):

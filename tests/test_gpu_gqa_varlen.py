@@ -270,3 +270,60 @@ def test_prefill_without_prefix_matches_varlen_forward():
     o2, lse2 = fa().forward_varlen(qd, k, v, cu, 333, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+# ------------------------------------------------------------ fused rotary
+@pytest.mark.parametrize("interleaved", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_rope_dense(causal, d, interleaved):
+    B, H, Hkv, N = 2, 4, 2, 300
+    q, k, v = workloads.gqa_inputs(B, H, Hkv, N, d, "bf16", seed=d + int(causal) + 2 * int(interleaved))
+    c, s = workloads.rope_tables(N + 5, d)
+    print(f"[rope] causal={causal} d={d} interleaved={interleaved}", flush=True)
+    o, lse = fa().forward_rope(*cuda(q, k, v, c, s), causal=causal, interleaved=interleaved)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_forward_rope(q, k, v, c, s, causal=causal, interleaved=interleaved)
+    check("rope O", to64(o), ro, BF16_MAX, BF16_MEAN)
+    check("rope LSE", to64(lse), rl, LSE_MAX)
+
+
+def test_forward_rope_long_positions():
+    """16K positions: angles up to 16383 rad in the fp32 tables."""
+    q, k, v = workloads.gqa_inputs(1, 2, 2, 16384, 128, "bf16", seed=31)
+    c, s = workloads.rope_tables(16384, 128)
+    o, lse = fa().forward_rope(*cuda(q, k, v, c, s), causal=True)
+    torch.cuda.synchronize()
+    rows = sorted(set([0, 1, 255, 256, 8191, 16383] + list(np.random.default_rng(3).integers(0, 16384, 24))))
+    pos = np.arange(16384)
+    qr = oracle.apply_rope_bf16(q, pos, c, s)
+    kr = oracle.apply_rope_bf16(k, pos, c, s)
+    for h in range(2):
+        ro, rl = oracle.attention_forward_rows(qr[0, h], kr[0, h], v[0, h], rows, causal=True)
+        check(f"rope 16K head {h} O", to64(o[0, h].cpu())[rows], ro, BF16_MAX, BF16_MEAN)
+        check(f"rope 16K head {h} LSE", to64(lse[0, h].cpu())[rows], rl, LSE_MAX)
+
+
+def test_forward_rope_varlen():
+    cu, q, k, v = workloads.varlen_inputs([300, 0, 1, 129, 64], 4, 1, 128, seed=41)
+    c, s = workloads.rope_tables(300, 128)
+    o, lse = fa().forward_rope(*cuda(q, k, v, c, s), causal=True, cu_seqlens=cu.to(DEV), max_seqlen=300)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_forward_rope(q, k, v, c, s, causal=True, cu_seqlens=cu)
+    check("rope varlen O", to64(o), ro, BF16_MAX, BF16_MEAN)
+    check("rope varlen LSE", to64(lse), rl, LSE_MAX)
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_prefill_paged_rope(interleaved):
+    p = workloads.prefill_inputs([300, 1, 64], [1000, 513, 64], H=8, Hkv=2, d=128, seed=5, poison=True,
+                                 spare_pages=2)
+    c, s = workloads.rope_tables(1024, 128)
+    qd, pool, bt, sl, cu = cuda(p.q, p.kv_pool, p.block_table, p.seq_lens_k, p.cu_seqlens_q)
+    o, lse = fa().prefill_paged(qd, pool, bt, sl, cu, 300, causal=True, rope_cos=c.to(DEV), rope_sin=s.to(DEV),
+                                rope_interleaved=interleaved)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill_paged(p.q, p.kv_pool, p.block_table, p.seq_lens_k, p.cu_seqlens_q, causal=True,
+                                  rope=(c, s, interleaved))
+    check("prefill rope O", to64(o), ro, BF16_MAX, BF16_MEAN)
+    check("prefill rope LSE", to64(lse), rl, LSE_MAX)

@@ -209,3 +209,13 @@ def prefill_inputs(chunk_lens, ctx_lens, H=32, Hkv=None, d=128, max_blocks=None,
     cu = torch.tensor([0] + list(itertools.accumulate(chunk_lens)), dtype=torch.int32)
     q = _draw(g, (int(cu[-1]), H, d), "bf16")
     return PrefillInputs(q, cu, p.kv_pool, p.block_table, torch.tensor(ctx_lens, dtype=torch.int32), page_size)
+
+
+def rope_tables(rows, d, base=10000.0):
+    """Rotary lookup tables (inputs, like the random draws): angle of pair i at
+    position p is p · base^(-2i/d); returns fp32 cos, sin [rows, d/2],
+    computed in fp64 and rounded once."""
+    import numpy as np
+    inv = base ** (-np.arange(0, d // 2, dtype=np.float64) * 2.0 / d)
+    ang = np.arange(rows, dtype=np.float64)[:, None] * inv[None, :]
+    return (torch.from_numpy(np.cos(ang)).to(torch.float32), torch.from_numpy(np.sin(ang)).to(torch.float32))
