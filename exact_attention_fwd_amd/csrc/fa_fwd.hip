@@ -66,6 +66,9 @@ __device__ __forceinline__ void map_unit(int bid, int B, int H, int& rank, int& 
 constexpr float kRescaleThreshold = 8.0f;
 
 constexpr int kPage = 256;  // tokens per page of a paged key/value pool
+#ifndef FWD_LOOK
+#define FWD_LOOK 2
+#endif
 
 // Rotate the feature pairs (x[j], y[j]) of 8 bf16 values each by the angles
 // whose cosines / sines are c[j], s[j]; bf16 (RNE) results.  Each product is
@@ -118,11 +121,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
   constexpr int ROWS_PER_DMA = 64 / CPR;      // rows per 1 KiB wavefront load
   constexpr int DMA_PER_WAVE = kTileRows / ROWS_PER_DMA / kWaves;
-  // K ring (2 tiles) then V ring (2 tiles), all row-major [64][D].  K runs one
+  // K ring (2 tiles) and V ring (2 tiles), all row-major [64][D].  K runs one
   // tile ahead of V: while tile t is consumed, K(t+1) is already resident.
-  __shared__ __attribute__((aligned(1024))) bf16 smem[4 * TILE];
-  bf16* const kring = smem;
-  bf16* const vring = smem + 2 * TILE;
+  // Each slot is its own LDS object and the loop below names slots at
+  // compile time, so the compiler can tell that reads of one slot do not
+  // depend on direct-to-LDS loads still in flight into another.
+  __shared__ __attribute__((aligned(1024))) bf16 kbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 kbuf1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 vbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 vbuf1[TILE];
   __shared__ int ptab[PAGED ? kMaxPrefillPages : 1];  // this sequence's pool pages
 
   const int tid = threadIdx.x;
@@ -241,30 +248,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     kdma[i] = (uint32_t)row * (kvs * 2) + ((dma_pc ^ rm_swz<D>(row)) << 4);
     vdma[i] = (uint32_t)row * (kvs * 2) + ((dma_pc ^ v_swz<D>(row)) << 4);
   }
-  auto issue_k = [&](int t) {
+  // Tile t of K (or V) into the given slot (t's parity: the caller names it).
+  auto issue_k = [&](bf16* slot, int t) {
     if constexpr (PAGED) {
       const auto r = page_rsrc(t, 0);
 #pragma unroll
-      for (int i = 0; i < DMA_PER_WAVE; ++i)
-        lds_dma16(r, kring + (t & 1) * TILE + (wave * DMA_PER_WAVE + i) * 512, kdma[i]);
+      for (int i = 0; i < DMA_PER_WAVE; ++i) lds_dma16(r, slot + (wave * DMA_PER_WAVE + i) * 512, kdma[i]);
     } else {
 #pragma unroll
       for (int i = 0; i < DMA_PER_WAVE; ++i)
-        lds_dma16(rk, kring + (t & 1) * TILE + (wave * DMA_PER_WAVE + i) * 512,
-                  kdma[i] + (uint32_t)t * (64 * kvs * 2));
+        lds_dma16(rk, slot + (wave * DMA_PER_WAVE + i) * 512, kdma[i] + (uint32_t)t * (64 * kvs * 2));
     }
   };
-  auto issue_v = [&](int t) {
+  auto issue_v = [&](bf16* slot, int t) {
     if constexpr (PAGED) {
       const auto r = page_rsrc(t, 1);
 #pragma unroll
-      for (int i = 0; i < DMA_PER_WAVE; ++i)
-        lds_dma16(r, vring + (t & 1) * TILE + (wave * DMA_PER_WAVE + i) * 512, vdma[i]);
+      for (int i = 0; i < DMA_PER_WAVE; ++i) lds_dma16(r, slot + (wave * DMA_PER_WAVE + i) * 512, vdma[i]);
     } else {
 #pragma unroll
       for (int i = 0; i < DMA_PER_WAVE; ++i)
-        lds_dma16(rv, vring + (t & 1) * TILE + (wave * DMA_PER_WAVE + i) * 512,
-                  vdma[i] + (uint32_t)t * (64 * kvs * 2));
+        lds_dma16(rv, slot + (wave * DMA_PER_WAVE + i) * 512, vdma[i] + (uint32_t)t * (64 * kvs * 2));
     }
   };
 
@@ -327,28 +331,29 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int wlast = min(qw + 31, N - 1) + off;  // causal: this wave's last visible key
   const int wnt = (qw >= N) ? 0 : (CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / kBC + 1)) : ntiles);
 
-  if (ntiles > 0) issue_k(0);
-  if (ntiles > 1) issue_k(1);
-  if (ntiles > 0) issue_v(0);
+  if (ntiles > 0) issue_k(kbuf0, 0);
+  if (ntiles > 1) issue_k(kbuf1, 1);
+  if (ntiles > 0) issue_v(vbuf0, 0);
   wait_vm_all();
   __syncthreads();
-  if (ntiles > 0) rope_k(kring, 0);
+  if (ntiles > 0) rope_k(kbuf0, 0);
   f32x16 sa[2], sb[2];
   if (wnt > 0) {
-    scores(kring, sa);
+    scores(kbuf0, sa);
     mask(0, sa);
     m_run = tile_max(sa);  // first tile: nothing to rescale yet
   }
 
   // One tile: P(t) from S(t) = sc, while S(t+1) = sn is computed on the matrix
   // pipe; then O += V(t)ᵀ P(t); then S(t+1) is masked and its max checked.
-  auto step = [&](int t, f32x16* sc, f32x16* sn) {
+  // kc / vc: the slots of tile t (parity of t); kn / vn: the other ones.
+  auto step = [&](int t, f32x16* sc, f32x16* sn, bf16* kc, bf16* kn, bf16* vc, bf16* vn) {
     const int k0 = t * kBC;
     wait_vm_all();
     __syncthreads();  // K(t+1) and V(t) resident for every wave; tile t-1 fully consumed
-    if (t + 2 < ntiles) issue_k(t + 2);
-    if (t + 1 < ntiles) issue_v(t + 1);
-    bf16* vs = vring + (t & 1) * TILE;
+    if (t + 2 < ntiles) issue_k(kc, t + 2);
+    if (t + 1 < ntiles) issue_v(vn, t + 1);
+    bf16* vs = vc;
     if (k0 + kBC > Nk) {  // tail tile: V rows past the last key must read as zero, whatever the loads left
       const int first = Nk - k0;
       for (int idx = tid; idx < (kBC - first) * CPR; idx += kThreads) {
@@ -357,55 +362,61 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       }
       __syncthreads();
     }
-    if (t + 1 < ntiles) rope_k(kring + ((t + 1) & 1) * TILE, (t + 1) * kBC);
+    if (t + 1 < ntiles) rope_k(kn, (t + 1) * kBC);
     if (t >= wnt) return;
 
-    // On a wave's last tile this product reads a stale K tile and is dropped.
-    scores(kring + ((t + 1) & 1) * TILE, sn);
-
+    // The tile runs as a fixed software pipeline of 2·KSTEPS + 4·DBLK slots,
+    // one matrix product each.  Slot i < 2·KSTEPS computes product i of
+    // S(t+1) = K(t+1)·Qᵀ (on a wave's last tile it reads a stale K tile and is
+    // dropped) and turns a slice of S(t) into probabilities on the VALU; the
+    // remaining slots accumulate Oᵀ += Vᵀ·Pᵀ.  Every LDS operand is read LOOK
+    // slots before the product that consumes it, so LDS latency overlaps the
+    // matrix pipe; the slot fences keep the compiler from undoing that order.
+    constexpr int LOOK = FWD_LOOK;
+    constexpr int NS = 2 * KSTEPS;  // products of S(t+1)
+    constexpr int NP = 4 * DBLK;    // products of Oᵀ += Vᵀ·Pᵀ
+    constexpr int PPS = 16 / NS;    // pairs of scores turned into probabilities per slot
+    auto kread = [&](int i) {  // K operand of S product i: key block i / KSTEPS, k-step i % KSTEPS
+      return *reinterpret_cast<const bf16x8*>(kn + (i / KSTEPS) * 32 * D + koff[i % KSTEPS]);
+    };
+    auto vread = [&](int j) {  // Vᵀ operand of P·V product j: d block j / 4, keys 16(j % 4)..
+      const bf16* base = vs + voff[j / 4] + 16 * (j % 4) * D;
+      const bf16x4 lo = lds_read_tr4(base);
+      const bf16x4 hi = lds_read_tr4(base + 4 * D);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    bf16x8 opk[LOOK + 1], opv[LOOK + 1];
+    u32x4 pw[4];  // P(t) as packed bf16 pairs: pw[2kb + h] holds keys 32kb + 16h ..
+#pragma unroll
+    for (int i = 0; i < LOOK; ++i) opk[i] = kread(i);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (i + LOOK < NS)
+        opk[(i + LOOK) % (LOOK + 1)] = kread(i + LOOK);
+      else
+        opv[i + LOOK - NS] = vread(i + LOOK - NS);
+      const int kb = i / KSTEPS, kk = i % KSTEPS;
+      sn[kb] = mfma32(opk[i % (LOOK + 1)], qreg[kk], kk == 0 ? f32x16{} : sn[kb]);
+#pragma unroll
+      for (int q = 0; q < PPS; ++q) {
+        const int pi = i * PPS + q;  // score pair: block pi / 8, rows 2(pi % 8), +1
+        const int pkb = pi / 8, r = 2 * (pi % 8);
+        const float p0 = exp2_fast(__builtin_fmaf(sc[pkb][r], scale_log2, -m_use));
+        const float p1 = exp2_fast(__builtin_fmaf(sc[pkb][r + 1], scale_log2, -m_use));
+        pw[2 * pkb + r / 8][(r % 8) / 2] = pack_bf16x2(p0, p1);
+        l_run += p0 + p1;  // fp32 sum of the unrounded p: the logsumexp needs it exact
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     bf16x8 pb[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int k = 0; k < 4; ++k) pb[k] = __builtin_bit_cast(bf16x8, pw[k]);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        u32x4 w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = exp2_fast(__builtin_fmaf(sc[kb][8 * h + 2 * j], scale_log2, -m_use));
-          const float p1 = exp2_fast(__builtin_fmaf(sc[kb][8 * h + 2 * j + 1], scale_log2, -m_use));
-          w[j] = pack_bf16x2(p0, p1);
-          l_run += p0 + p1;  // fp32 sum of the unrounded p: the logsumexp needs it exact
-        }
-        pb[2 * kb + h] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
-
-    // Oᵀ += Vᵀ Pᵀ (Vᵀ read transposed out of the row-major tile)
-#pragma unroll
-    for (int b = 0; b < DBLK; ++b) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16* base = vs + voff[b] + 16 * kk * D;
-        const bf16x4 lo = lds_read_tr4(base);
-        const bf16x4 hi = lds_read_tr4(base + 4 * D);
-        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[b] = mfma32(a, pb[kk], oacc[b]);
-      }
-    }
-    // Interleave: each S(t+1) product with a K read and a slice of the
-    // softmax VALU work, then the P·V products with their transposed reads.
-#pragma unroll
-    for (int i = 0; i < 2 * KSTEPS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // VALU
-    }
-#pragma unroll
-    for (int i = 0; i < 4 * DBLK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS transposed reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU
+    for (int j = 0; j < NP; ++j) {
+      if (j + LOOK < NP) opv[(j + LOOK) % (LOOK + 1)] = vread(j + LOOK);
+      oacc[j / 4] = mfma32(opv[j % (LOOK + 1)], pb[j % 4], oacc[j / 4]);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // Move the reference max for tile t+1 if it grew too far (O now holds tile t).
@@ -426,8 +437,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   };
 
   for (int t = 0; t < ntiles; t += 2) {  // unrolled by two so S(t) and S(t+1) swap registers
-    step(t, sa, sb);
-    if (t + 1 < ntiles) step(t + 1, sb, sa);
+    step(t, sa, sb, kbuf0, kbuf1, vbuf0, vbuf1);
+    if (t + 1 < ntiles) step(t + 1, sb, sa, kbuf1, kbuf0, vbuf1, vbuf0);
   }
 
   if (qw >= N || qrow >= N) return;
