@@ -23,6 +23,8 @@
 // (ai.lansai.wang), 技术原理 › 核心工作机制 (tiling into on-chip memory and
 // the online softmax) and 关键术语解析 §4 (the running max m and normaliser l
 // updates); zwxr.cn §3.1 (rescale by the final normaliser once at the end).
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -59,6 +61,13 @@ __device__ __forceinline__ void map_unit(int bid, int B, int H, int& rank, int& 
   h = u / B;
 }
 
+// m = max(m, a, b) as one v_max3_f32 that stays where it is written: work
+// scheduled into a pipeline slot must not be sunk out of it into the branch
+// that consumes it.
+__device__ __forceinline__ void max3_here(float& m, float a, float b) {
+  asm volatile("v_max3_f32 %0, %0, %1, %2" : "+v"(m) : "v"(a), "v"(b));
+}
+
 // Rescale the output only when the running max grows by more than this many
 // powers of two.  Between rescales p = 2^(s·scale·log2e − m) <= 2^8: the
 // output, its normaliser and the logsumexp all use the same reference m, so
@@ -68,6 +77,9 @@ constexpr float kRescaleThreshold = 8.0f;
 constexpr int kPage = 256;  // tokens per page of a paged key/value pool
 #ifndef FWD_LOOK
 #define FWD_LOOK 2
+#endif
+#ifndef FWD_W64
+#define FWD_W64 1
 #endif
 
 // Rotate the feature pairs (x[j], y[j]) of 8 bf16 values each by the angles
@@ -346,83 +358,83 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   // One tile: P(t) from S(t) = sc, while S(t+1) = sn is computed on the matrix
   // pipe; then O += V(t)ᵀ P(t); then S(t+1) is masked and its max checked.
-  // kc / vc: the slots of tile t (parity of t); kn / vn: the other ones.
-  auto step = [&](int t, f32x16* sc, f32x16* sn, bf16* kc, bf16* kn, bf16* vc, bf16* vn) {
-    const int k0 = t * kBC;
-    wait_vm_all();
-    __syncthreads();  // K(t+1) and V(t) resident for every wave; tile t-1 fully consumed
-    if (t + 2 < ntiles) issue_k(kc, t + 2);
-    if (t + 1 < ntiles) issue_v(vn, t + 1);
-    bf16* vs = vc;
-    if (k0 + kBC > Nk) {  // tail tile: V rows past the last key must read as zero, whatever the loads left
-      const int first = Nk - k0;
-      for (int idx = tid; idx < (kBC - first) * CPR; idx += kThreads) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(vs + (first + idx / CPR) * D + (idx % CPR) * 8) = z;
-      }
-      __syncthreads();
-    }
-    if (t + 1 < ntiles) rope_k(kn, (t + 1) * kBC);
-    if (t >= wnt) return;
-
-    // The tile runs as a fixed software pipeline of 2·KSTEPS + 4·DBLK slots,
-    // one matrix product each.  Slot i < 2·KSTEPS computes product i of
-    // S(t+1) = K(t+1)·Qᵀ (on a wave's last tile it reads a stale K tile and is
-    // dropped) and turns a slice of S(t) into probabilities on the VALU; the
-    // remaining slots accumulate Oᵀ += Vᵀ·Pᵀ.  Every LDS operand is read LOOK
-    // slots before the product that consumes it, so LDS latency overlaps the
-    // matrix pipe; the slot fences keep the compiler from undoing that order.
-    constexpr int LOOK = FWD_LOOK;
-    constexpr int NS = 2 * KSTEPS;  // products of S(t+1)
-    constexpr int NP = 4 * DBLK;    // products of Oᵀ += Vᵀ·Pᵀ
-    constexpr int PPS = 16 / NS;    // pairs of scores turned into probabilities per slot
+  // One tile as a fixed software pipeline of NS + NP fenced slots, one matrix
+  // product each.  Slots 0 .. NS-1 compute S(t+1) = K(t+1)·Qᵀ (on a wave's last
+  // tile they read a stale K tile and are dropped); slots NS .. NS+NP-1
+  // accumulate Oᵀ += Vᵀ·Pᵀ, key chunk by key chunk.  The VALU work rides
+  // along: the 16 pairs of S(t) scores become bf16 probabilities in the first
+  // slots (pair pi by slot pi·SPAN/16, before the product that first needs
+  // its chunk), and the last slots take the max of S(t+1).  A diagonal or
+  // tail tile (maskn) is masked and its max retaken after the slots.  Every
+  // LDS operand is read LOOK slots ahead of its product; the fences keep the
+  // compiler from undoing the order.
+  constexpr int LOOK = FWD_LOOK;
+  constexpr int NS = 2 * KSTEPS;     // products of S(t+1)
+  constexpr int NP = 4 * DBLK;       // products of Oᵀ += Vᵀ·Pᵀ
+  constexpr int NT = NS + NP;
+  constexpr int SPAN = NS + 3 * DBLK - 2;
+  constexpr int MAX0 = NS + 2;       // first slot that reads S(t+1)
+  auto tile_slots = [&](bool maskn, int t, f32x16* sc, f32x16* sn, const bf16* kn, const bf16* vs) {
     auto kread = [&](int i) {  // K operand of S product i: key block i / KSTEPS, k-step i % KSTEPS
       return *reinterpret_cast<const bf16x8*>(kn + (i / KSTEPS) * 32 * D + koff[i % KSTEPS]);
     };
-    auto vread = [&](int j) {  // Vᵀ operand of P·V product j: d block j / 4, keys 16(j % 4)..
-      const bf16* base = vs + voff[j / 4] + 16 * (j % 4) * D;
+    auto vread = [&](int j) {  // Vᵀ operand of P·V product j: key chunk j / DBLK, d block j % DBLK
+      const bf16* base = vs + voff[j % DBLK] + 16 * (j / DBLK) * D;
       const bf16x4 lo = lds_read_tr4(base);
       const bf16x4 hi = lds_read_tr4(base + 4 * D);
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-    bf16x8 opk[LOOK + 1], opv[LOOK + 1];
+    bf16x8 op[LOOK + 1];
     u32x4 pw[4];  // P(t) as packed bf16 pairs: pw[2kb + h] holds keys 32kb + 16h ..
+    float mx = kNegInf;
 #pragma unroll
-    for (int i = 0; i < LOOK; ++i) opk[i] = kread(i);
+    for (int i = 0; i < LOOK; ++i) op[i] = kread(i);
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      if (i + LOOK < NS)
-        opk[(i + LOOK) % (LOOK + 1)] = kread(i + LOOK);
-      else
-        opv[i + LOOK - NS] = vread(i + LOOK - NS);
-      const int kb = i / KSTEPS, kk = i % KSTEPS;
-      sn[kb] = mfma32(opk[i % (LOOK + 1)], qreg[kk], kk == 0 ? f32x16{} : sn[kb]);
+    for (int sl = 0; sl < NT; ++sl) {
+      // operand read for the product LOOK slots ahead
+      const int ahead = sl + LOOK;
+      if (ahead < NS)
+        op[ahead % (LOOK + 1)] = kread(ahead);
+      else if (ahead < NT)
+        op[ahead % (LOOK + 1)] = vread(ahead - NS);
+      // this slot's product
+      if (sl < NS) {
+        const int kb = sl / KSTEPS, kk = sl % KSTEPS;
+        sn[kb] = mfma32(op[sl % (LOOK + 1)], qreg[kk], kk == 0 ? f32x16{} : sn[kb]);
+      } else {
+        const int j = sl - NS;
+        const int kk = j / DBLK, b = j % DBLK;
+        oacc[b] = mfma32(op[sl % (LOOK + 1)], __builtin_bit_cast(bf16x8, pw[kk]), oacc[b]);
+      }
+      // probabilities of S(t) for the pairs scheduled here
 #pragma unroll
-      for (int q = 0; q < PPS; ++q) {
-        const int pi = i * PPS + q;  // score pair: block pi / 8, rows 2(pi % 8), +1
+      for (int pi = 0; pi < 16; ++pi) {
+        if ((pi * SPAN) / 16 != sl) continue;
         const int pkb = pi / 8, r = 2 * (pi % 8);
         const float p0 = exp2_fast(__builtin_fmaf(sc[pkb][r], scale_log2, -m_use));
         const float p1 = exp2_fast(__builtin_fmaf(sc[pkb][r + 1], scale_log2, -m_use));
         pw[2 * pkb + r / 8][(r % 8) / 2] = pack_bf16x2(p0, p1);
         l_run += p0 + p1;  // fp32 sum of the unrounded p: the logsumexp needs it exact
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    bf16x8 pb[4];
+      // max of S(t+1) for the values scheduled here
 #pragma unroll
-    for (int k = 0; k < 4; ++k) pb[k] = __builtin_bit_cast(bf16x8, pw[k]);
-#pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      if (j + LOOK < NP) opv[(j + LOOK) % (LOOK + 1)] = vread(j + LOOK);
-      oacc[j / 4] = mfma32(opv[j % (LOOK + 1)], pb[j % 4], oacc[j / 4]);
+      for (int v = 0; v < 32; v += 2) {
+        if (MAX0 + (v * (NT - MAX0)) / 32 != sl) continue;
+        max3_here(mx, sn[v / 16][v % 16], sn[v / 16][v % 16 + 1]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 
     // Move the reference max for tile t+1 if it grew too far (O now holds tile t).
     if (t + 1 < wnt) {
-      mask(k0 + kBC, sn);
-      const float mx = tile_max(sn);
+      if (maskn) {
+        mask((t + 1) * kBC, sn);
+        mx = kNegInf;
+#pragma unroll
+        for (int v = 0; v < 32; ++v) mx = fmaxf(mx, sn[v / 16][v % 16]);
+      }
+      mx = xhalf_max(mx) * scale_log2;
       if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = exp2_fast(m_run - m_new);
@@ -434,6 +446,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         m_run = m_new;
       }
     }
+  };
+
+  // kc / vc: the slots of tile t (parity of t); kn / vn: the other ones.
+  auto step = [&](int t, f32x16* sc, f32x16* sn, bf16* kc, bf16* kn, bf16* vc, bf16* vn) {
+    const int k0 = t * kBC;
+    wait_vm_all();
+    __syncthreads();  // K(t+1) and V(t) resident for every wave; tile t-1 fully consumed
+    if (t + 2 < ntiles) issue_k(kc, t + 2);
+    if (t + 1 < ntiles) issue_v(vn, t + 1);
+    if (k0 + kBC > Nk) {  // tail tile: V rows past the last key must read as zero, whatever the loads left
+      const int first = Nk - k0;
+      for (int idx = tid; idx < (kBC - first) * CPR; idx += kThreads) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(vc + (first + idx / CPR) * D + (idx % CPR) * 8) = z;
+      }
+      __syncthreads();
+    }
+    if (t + 1 < ntiles) rope_k(kn, (t + 1) * kBC);
+    if (t >= wnt) return;
+    const int k0n = k0 + kBC;
+    tile_slots((CAUSAL && k0n + kBC - 1 > qw + off) || (k0n + kBC > Nk), t, sc, sn, kn, vc);
   };
 
   for (int t = 0; t < ntiles; t += 2) {  // unrolled by two so S(t) and S(t+1) swap registers
@@ -457,6 +490,343 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       *reinterpret_cast<u32x2*>(Orow + 32 * b + 8 * i + 4 * g) = w;
     }
   if (LSE != nullptr && g == 0) LSE[hv.st_off + qrow] = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : kNegInf;
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Matrix products of the 64-query kernel, written as single instructions so
+// that each operand sits in the register file it is used from: score blocks
+// in VGPRs (the VALU reads them), the output accumulators and Qᵀ in AGPRs
+// (only the matrix unit touches them).  The compiler cannot see the latency
+// of these instructions: a VALU read of their results that is not already
+// separated by later slots is preceded by mfma_drain().
+__device__ __forceinline__ void mfma_s0(f32x16& s, const bf16x8& a, const bf16x8& q) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "a"(q));
+}
+__device__ __forceinline__ void mfma_s(f32x16& s, const bf16x8& a, const bf16x8& q) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "a"(q));
+}
+__device__ __forceinline__ void mfma_o(f32x16& o, const bf16x8& a, const bf16x8& p) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(p));
+}
+// x *= alpha for a value held in an accumulation register.
+__device__ __forceinline__ void acc_scale(float& x, float alpha) {
+  float t;
+  asm("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+      : "+a"(x), "=&v"(t)
+      : "v"(alpha));
+}
+// More wait states than a 32x32x16 product needs before its result is read.
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+// The same forward with 64 queries per wavefront, for d = 128 with K/V laid
+// out like the queries (dense, grouped heads, packed batches): four
+// wavefronts per workgroup, one per SIMD.  Each K and Vᵀ operand read from
+// LDS feeds two products (query blocks j = 0, 1), halving LDS traffic per
+// FLOP; the output accumulators live in accumulation registers.
+template <bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                                                         const bf16* __restrict__ V, bf16* __restrict__ O,
+                                                         float* __restrict__ LSE, AttnShape shape,
+                                                         float scale_log2) {
+  constexpr int D = 128;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DBLK = D / 32;
+  constexpr int TILE = kTileRows * D;
+  constexpr int CPR = D / 8;
+  constexpr int WAVES = 4;
+  constexpr int THREADS = 64 * WAVES;
+  constexpr int ROWS_PER_DMA = 64 / CPR;
+  constexpr int DMA_PER_WAVE = kTileRows / ROWS_PER_DMA / WAVES;
+  __shared__ __attribute__((aligned(1024))) bf16 kbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 kbuf1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 vbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 vbuf1[TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, n = lane & 31;
+  int rank, bi, hi;
+  map_unit(blockIdx.x, shape.B, shape.H, rank, bi, hi);
+  const HeadView hv = head_view(shape, bi, hi, D);
+  const int N = hv.L;
+  const int nqb = (N + kBR - 1) / kBR;
+  if (rank >= nqb) return;
+  const int qb = CAUSAL ? nqb - 1 - rank : rank;
+  const int q0 = qb * kBR;
+  const int Nk = N;
+  const int kvs = hv.kvs;
+  const auto rq = make_rsrc(Q + hv.q_off, (uint32_t)N * hv.qs * 2);
+  const auto rk = make_rsrc(K + hv.kv_off, (uint32_t)N * hv.kvs * 2);
+  const auto rv = make_rsrc(V + hv.kv_off, (uint32_t)N * hv.kvs * 2);
+  const int qw = q0 + wave * 64;  // this wave's first query; query block j holds qw + 32j ..
+
+  // Qᵀ as the B operand of both query blocks (zeros past N).
+  bf16x8 qreg[2][KSTEPS];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      qreg[j][kk] = __builtin_bit_cast(
+          bf16x8, buf_load16(rq, (uint32_t)(qw + 32 * j + n) * (hv.qs * 2) + (16 * kk + 8 * g) * 2));
+
+  // Direct-to-LDS loads: rows (wave·DMA_PER_WAVE + i)·ROWS_PER_DMA + lane / CPR
+  // of a tile; the swizzled chunk offsets are recomputed at each issue.
+  const int dma_row = lane / CPR, dma_pc = lane % CPR;
+  auto dma_off = [&](int i, bool vtile) {
+    const int row = (wave * DMA_PER_WAVE + i) * ROWS_PER_DMA + dma_row;
+    return (uint32_t)row * (kvs * 2) + ((dma_pc ^ (vtile ? v_swz<D>(row) : rm_swz<D>(row))) << 4);
+  };
+  auto issue_k = [&](bf16* slot, int t) {
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i)
+      lds_dma16(rk, slot + (wave * DMA_PER_WAVE + i) * 512, dma_off(i, false) + (uint32_t)t * (64 * kvs * 2));
+  };
+  auto issue_v = [&](bf16* slot, int t) {
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i)
+      lds_dma16(rv, slot + (wave * DMA_PER_WAVE + i) * 512, dma_off(i, true) + (uint32_t)t * (64 * kvs * 2));
+  };
+
+  // LDS operand offsets (elements).  K: rows perm_row(n), 16-byte chunk
+  // (2kk + g) ^ (n % 16) = 2(kk ^ c1) + (g ^ c0) with c = n % 16: one base and
+  // an XOR per k-step.  Vᵀ: chunk (4b + x) ^ v_swz(row) with x < 4 is
+  // 4(b ^ s2) + (x ^ (v_swz & 3)), s2 = v_swz >> 2: one base and an XOR per d block.
+  const int kc = n & (CPR - 1);
+  const int kbase = perm_row(n) * D + ((g ^ (kc & 1)) << 3);
+  const int kx = (kc >> 1) << 4;
+  auto koff = [&](int kk) { return kbase + ((kk << 4) ^ kx); };
+  const int G = lane >> 4, j16 = lane & 15;
+  const int vrow = 8 * (G >> 1) + (j16 >> 2);
+  const int vsw = v_swz<D>(vrow);
+  const int vx = 2 * (G & 1) + ((4 * (j16 & 3)) >> 3);
+  const int vbase = vrow * D + ((vx ^ (vsw & 3)) << 3) + ((4 * (j16 & 3)) & 7);
+  const int vs2 = (vsw >> 2) << 5;
+  auto voff = [&](int b) { return vbase + ((b << 5) ^ vs2); };
+
+  // s[2 kb + j]: Sᵀ block of keys 32kb.., queries 32j.. (register r: key crow(kb, r, g), query n).
+  auto mask = [&](int k0, f32x16* s) {
+    if ((CAUSAL && k0 + kBC - 1 > qw) || (k0 + kBC > Nk)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + crow(kb, r, g);
+            const bool dead = (key >= Nk) || (CAUSAL && key > qw + 32 * j + n);
+            s[2 * kb + j][r] = dead ? kNegInf : s[2 * kb + j][r];
+          }
+    }
+  };
+
+  f32x16 oacc[DBLK][2];
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[b][j][r] = 0.f;
+  float m_run[2] = {kNegInf, kNegInf};
+  float l_run[2] = {0.f, 0.f};
+
+  const int kv_end = CAUSAL ? min(Nk, q0 + kBR) : Nk;
+  const int ntiles = (kv_end + kBC - 1) / kBC;
+  const int wlast = min(qw + 63, N - 1);
+  const int wnt = (qw >= N) ? 0 : (CAUSAL ? min(ntiles, wlast / kBC + 1) : ntiles);
+
+  if (ntiles > 0) issue_k(kbuf0, 0);
+  if (ntiles > 1) issue_k(kbuf1, 1);
+  if (ntiles > 0) issue_v(vbuf0, 0);
+  wait_vm_all();
+  __syncthreads();
+  f32x16 sa[4], sb[4];
+  if (wnt > 0) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbuf0 + kb * 32 * D + koff(kk));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (kk == 0)
+            mfma_s0(sa[2 * kb + j], a, qreg[j][kk]);
+          else
+            mfma_s(sa[2 * kb + j], a, qreg[j][kk]);
+        }
+      }
+    mfma_drain();
+    mask(0, sa);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[2 * kb + j][r]);
+      m_run[j] = xhalf_max(mx) * scale_log2;
+    }
+  }
+
+  // One tile: NS slots of S(t+1) (one K read, two products each), then NP
+  // slots of Oᵀ += Vᵀ·Pᵀ (one Vᵀ read, two products each); P(t) pairs and
+  // the max of S(t+1) ride along as in the 32-query kernel.
+  constexpr int LOOK = FWD_LOOK;
+  constexpr int NS = 2 * KSTEPS;
+  constexpr int NP = 4 * DBLK;
+  constexpr int NT = NS + NP;
+  constexpr int SPAN = NS + 3 * DBLK - 2;
+  constexpr int MAX0 = NS + 2;
+  auto tile_slots = [&](bool maskn, int t, f32x16* sc, f32x16* sn, const bf16* kn, const bf16* vs) {
+    auto kread = [&](int i) {
+      return *reinterpret_cast<const bf16x8*>(kn + (i / KSTEPS) * 32 * D + koff(i % KSTEPS));
+    };
+    auto vread = [&](int jj) {  // Vᵀ operand: key chunk jj / DBLK, d block jj % DBLK
+      const bf16* base = vs + voff(jj % DBLK) + 16 * (jj / DBLK) * D;
+      const bf16x4 lo = lds_read_tr4(base);
+      const bf16x4 hi = lds_read_tr4(base + 4 * D);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    float m_use[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) m_use[j] = (m_run[j] == kNegInf) ? 0.f : m_run[j];
+    bf16x8 op[LOOK + 1];
+    u32x4 pw[2][4];  // P(t) of query block j, keys 16kk .. as packed bf16 pairs
+    float mx[2] = {kNegInf, kNegInf};
+    static_for<0, LOOK>([&](auto ic) __attribute__((always_inline)) { op[ic.value] = kread(ic.value); });
+    // Half-slots: one product each, so that with one wavefront per SIMD the
+    // VALU work issues between consecutive products instead of waiting behind
+    // a second one for the matrix pipe.
+    static_for<0, 2 * NT>([&](auto hc) __attribute__((always_inline)) {
+      constexpr int hs = decltype(hc)::value;
+      constexpr int sl = hs / 2, j = hs % 2;
+      constexpr int ahead = sl + LOOK;
+      if constexpr (j == 0) {
+        if constexpr (ahead < NS)
+          op[ahead % (LOOK + 1)] = kread(ahead);
+        else if constexpr (ahead < NT)
+          op[ahead % (LOOK + 1)] = vread(ahead - NS);
+      }
+      if constexpr (sl < NS) {
+        constexpr int kb = sl / KSTEPS, kk = sl % KSTEPS;
+        if constexpr (kk == 0)
+          mfma_s0(sn[2 * kb + j], op[sl % (LOOK + 1)], qreg[j][kk]);
+        else
+          mfma_s(sn[2 * kb + j], op[sl % (LOOK + 1)], qreg[j][kk]);
+      } else {
+        constexpr int jj = sl - NS;
+        constexpr int kk = jj / DBLK, b = jj % DBLK;
+        mfma_o(oacc[b][j], op[sl % (LOOK + 1)], __builtin_bit_cast(bf16x8, pw[j][kk]));
+      }
+      // score pairs: pi = 8 kk + 4 jp + w  (kk = key chunk, jp = query block, w = pair inside it)
+      static_for<0, 32>([&](auto pic) __attribute__((always_inline)) {
+        constexpr int pi = decltype(pic)::value;
+        if constexpr ((pi * SPAN) / 16 == hs) {
+          constexpr int kk = pi / 8, jp = (pi / 4) % 2, w = pi % 4;
+          constexpr int kb = kk / 2, r = 8 * (kk % 2) + 2 * w;
+          const float p0 = exp2_fast(__builtin_fmaf(sc[2 * kb + jp][r], scale_log2, -m_use[jp]));
+          const float p1 = exp2_fast(__builtin_fmaf(sc[2 * kb + jp][r + 1], scale_log2, -m_use[jp]));
+          pw[jp][kk][w] = pack_bf16x2(p0, p1);
+          l_run[jp] += p0 + p1;
+        }
+      });
+      static_for<0, 32>([&](auto vc_) __attribute__((always_inline)) {
+        constexpr int v = 2 * decltype(vc_)::value;  // values v, v+1 of S(t+1)
+        if constexpr (2 * MAX0 + (v * 2 * (NT - MAX0)) / 64 == hs) {
+          constexpr int blk = v / 16;  // block 2kb + j
+          max3_here(mx[blk % 2], sn[blk][v % 16], sn[blk][v % 16 + 1]);
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+
+    if (t + 1 < wnt) {
+      if (maskn) {
+        mask((t + 1) * kBC, sn);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          mx[j] = kNegInf;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx[j] = fmaxf(mx[j], sn[2 * kb + j][r]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float m = xhalf_max(mx[j]) * scale_log2;
+        if (__builtin_amdgcn_ballot_w64(m > m_run[j] + kRescaleThreshold)) {
+          mfma_drain();
+          const float m_new = fmaxf(m_run[j], m);
+          const float alpha = exp2_fast(m_run[j] - m_new);
+          l_run[j] *= alpha;
+          // in place in the accumulation registers, one element at a time
+#pragma unroll
+          for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              float x = oacc[b][j][r];
+              acc_scale(x, alpha);
+              oacc[b][j][r] = x;
+            }
+          m_run[j] = m_new;
+        }
+      }
+    }
+  };
+
+  auto step = [&](int t, f32x16* sc, f32x16* sn, bf16* kc, bf16* kn, bf16* vc, bf16* vn) {
+    const int k0 = t * kBC;
+    wait_vm_all();
+    __syncthreads();  // K(t+1) and V(t) resident for every wave; tile t-1 fully consumed
+    if (t + 2 < ntiles) issue_k(kc, t + 2);
+    if (t + 1 < ntiles) issue_v(vn, t + 1);
+    if (k0 + kBC > Nk) {  // tail tile: V rows past the last key must read as zero
+      const int first = Nk - k0;
+      for (int idx = tid; idx < (kBC - first) * CPR; idx += THREADS) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(vc + (first + idx / CPR) * D + (idx % CPR) * 8) = z;
+      }
+      __syncthreads();
+    }
+    if (t >= wnt) return;
+    const int k0n = k0 + kBC;
+    tile_slots((CAUSAL && k0n + kBC - 1 > qw) || (k0n + kBC > Nk), t, sc, sn, kn, vc);
+  };
+
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, sa, sb, kbuf0, kbuf1, vbuf0, vbuf1);
+    if (t + 1 < ntiles) step(t + 1, sb, sa, kbuf1, kbuf0, vbuf1, vbuf0);
+  }
+  mfma_drain();
+
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int qrow = qw + 32 * j + n;
+    if (qrow >= N) continue;
+    const float l_tot = xhalf_sum(l_run[j]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    bf16* Orow = O + hv.q_off + (size_t)qrow * hv.qs;
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[b][j][4 * i + 0] * inv, oacc[b][j][4 * i + 1] * inv);
+        w[1] = pack_bf16x2(oacc[b][j][4 * i + 2] * inv, oacc[b][j][4 * i + 3] * inv);
+        *reinterpret_cast<u32x2*>(Orow + 32 * b + 8 * i + 4 * g) = w;
+      }
+    if (LSE != nullptr && g == 0)
+      LSE[hv.st_off + qrow] = l_tot > 0.f ? (m_run[j] + log2_fast(l_tot)) * kLn2 : kNegInf;
+  }
 }
 
 // fp32 path: one thread per query row, keys staged through LDS 32 at a time,
@@ -537,9 +907,27 @@ hipError_t launch_bf16(const ForwardArgs& a) {
   return hipGetLastError();
 }
 
+hipError_t launch_w64(const ForwardArgs& a) {
+  const int nqb = (a.s.N + kBR - 1) / kBR;
+  const dim3 grid((unsigned)(nqb * a.s.B * a.s.H)), block(256);
+  const float sl2 = a.scale * kLog2e;
+  auto* q = static_cast<const bf16*>(a.q);
+  auto* k = static_cast<const bf16*>(a.k);
+  auto* v = static_cast<const bf16*>(a.v);
+  auto* o = static_cast<bf16*>(a.o);
+  if (a.causal)
+    hipLaunchKernelGGL((fwd_w64_kernel<true>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.s, sl2);
+  else
+    hipLaunchKernelGGL((fwd_w64_kernel<false>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.s, sl2);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_bf16_any(const ForwardArgs& a) {
   const bool paged = a.kv.pool != nullptr, rope = a.rope.cos != nullptr;
+#if FWD_W64
+  if (D == 128 && !paged && !rope) return launch_w64(a);
+#endif
   if (paged) return rope ? launch_bf16<D, true, true>(a) : launch_bf16<D, true, false>(a);
   return rope ? launch_bf16<D, false, true>(a) : launch_bf16<D, false, false>(a);
 }
