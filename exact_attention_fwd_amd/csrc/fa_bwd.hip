@@ -30,6 +30,10 @@ namespace {
 
 constexpr int kThreads = 256;
 
+#ifndef BWD_PIPE
+#define BWD_PIPE 1
+#endif
+
 // Linear block id -> (tile rank, batch entry, head).  Blocks go round-robin
 // over the 8 XCDs (XCD x runs the ids with id % 8 == x).  Units are numbered
 // head-major (u = h·B + b) and each XCD takes a contiguous range of them, so
@@ -110,34 +114,41 @@ struct TileDma {
 };
 
 // Per-lane element offsets of the two operand reads of a dual-swizzled tile.
+// The second half of a transposed read (rows +4) sits at the same per-lane
+// distance from the first for every d block, so one delta is kept.
 template <int D>
 struct TileReads {
   static constexpr int KSTEPS = D / 16, DBLK = D / 32;
-  int rm[KSTEPS];     // row-major A operand: row perm_row(n) (+32 kb), chunk 2kk+g
-  int tr[DBLK][2];    // transposed A operand: rows 8(G>>1) + 4c + j/4 (+16 kk), column 32b + 16(G&1) + 4(j%4)
+  // row-major A operand: row perm_row(n) (+32 kb), chunk (2kk + g) ^ s with
+  // s = dual_swz(row), i.e. 2(kk ^ s/2) + (g ^ s%2): a base and an XOR per k-step
+  int rmb, rmx;
+  int tr[DBLK];    // transposed A operand, first half: rows 8(G>>1) + j/4 (+16 kk), column 32b + 16(G&1) + 4(j%4)
+  int trd;         // second half (rows +4) minus first half
   __device__ __forceinline__ void init(int lane) {
     const int g = lane >> 5, n = lane & 31;
     const int pr = perm_row(n);
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) rm[kk] = pr * D + (((2 * kk + g) ^ dual_swz<D>(pr)) << 3);
+    const int sw = dual_swz<D>(pr);
+    rmb = pr * D + ((g ^ (sw & 1)) << 3);
+    rmx = (sw >> 1) << 4;
     const int G = lane >> 4, j = lane & 15;
+    auto off = [&](int b, int c) {
+      const int row = 8 * (G >> 1) + 4 * c + (j >> 2);
+      const int col = 32 * b + 16 * (G & 1) + 4 * (j & 3);
+      return row * D + (((col >> 3) ^ dual_swz<D>(row)) << 3) + (col & 7);
+    };
 #pragma unroll
-    for (int b = 0; b < DBLK; ++b)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int row = 8 * (G >> 1) + 4 * c + (j >> 2);
-        const int col = 32 * b + 16 * (G & 1) + 4 * (j & 3);
-        tr[b][c] = row * D + (((col >> 3) ^ dual_swz<D>(row)) << 3) + (col & 7);
-      }
+    for (int b = 0; b < DBLK; ++b) tr[b] = off(b, 0);
+    trd = off(0, 1) - off(0, 0);
   }
   // rows 32kb.. of the tile, k-step kk over the head dim
   __device__ __forceinline__ bf16x8 row_major(const bf16* tile, int kb, int kk) const {
-    return *reinterpret_cast<const bf16x8*>(tile + kb * 32 * D + rm[kk]);
+    return *reinterpret_cast<const bf16x8*>(tile + kb * 32 * D + rmb + ((kk << 4) ^ rmx));
   }
   // head-dim rows 32b.., k-step kk over the tile's rows (16kk .. 16kk+15)
   __device__ __forceinline__ bf16x8 transposed(const bf16* tile, int b, int kk) const {
-    const bf16x4 lo = lds_read_tr4(tile + tr[b][0] + 16 * kk * D);
-    const bf16x4 hi = lds_read_tr4(tile + tr[b][1] + 16 * kk * D);
+    const bf16* p = tile + tr[b] + 16 * kk * D;
+    const bf16x4 lo = lds_read_tr4(p);
+    const bf16x4 hi = lds_read_tr4(p + trd);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 };
@@ -332,6 +343,237 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV for d = 128 as a software pipeline: one wavefront of 32 keys per
+// SIMD, four per workgroup.  Step t runs 64 half-slots, one matrix product
+// each: the first 32 compute S(t+1) = Q·Kᵀ and dP(t+1) = dO·Vᵀ of the next
+// 64-query tile, the last 32 accumulate dVᵀ += dOᵀ·P(t) and dKᵀ += Qᵀ·dS(t);
+// meanwhile the VALU turns S(t), dP(t) into P = 2^(s·scale·log2e −
+// LSE·log2e) and dS = P ∘ (dP − D).  Every LDS operand is read LOOK
+// half-slots ahead of its product.  Q/dO tiles and their LSE/D rows stream
+// through a four-slot LDS ring three tiles ahead (each slot its own LDS
+// object, named statically, so reads never wait on loads into other
+// slots); K, V and the dK, dV accumulators stay in AGPRs.  Diagonal and tail
+// tiles are masked once, on S(t), dP(t), before their step.
+// ---------------------------------------------------------------------------
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+    bf16* __restrict__ dK, bf16* __restrict__ dV, AttnShape shape, float scale, float scale_log2) {
+  constexpr int D = 128;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DBLK = D / 32;
+  constexpr int TILE = kTileRows * D;
+  constexpr int NA = 2 * 2 * KSTEPS;  // S and dP products of a tile (two 32-query blocks)
+  constexpr int NT = 2 * NA;          // plus as many dV and dK products
+  constexpr int LOOK = 2;
+  constexpr int VMEM_PER_TILE = 2 * TileDma<D>::DPW + 1;  // Q, dO blocks and one statistics load per wave
+  __shared__ __attribute__((aligned(1024))) bf16 qs0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 qs1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 qs2[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 qs3[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 ds0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 ds1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 ds2[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 ds3[TILE];
+  // statistics of a tile: LSE of its 64 query rows, then D of those rows
+  __shared__ __attribute__((aligned(16))) float ss0[2 * kTileRows];
+  __shared__ __attribute__((aligned(16))) float ss1[2 * kTileRows];
+  __shared__ __attribute__((aligned(16))) float ss2[2 * kTileRows];
+  __shared__ __attribute__((aligned(16))) float ss3[2 * kTileRows];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, n = lane & 31;
+  int rank, b, hkv;
+  map_unit(blockIdx.x, shape.B, shape.Hkv, rank, b, hkv);
+  const int group = shape.H / shape.Hkv;
+  const HeadView kv = head_view(shape, b, hkv * group, D);
+  const int N = kv.L;
+  const int k0 = rank * 128;
+  if (k0 >= N) return;
+  const int kw = k0 + 32 * wave;
+  const int key = kw + n;
+  const auto rk = make_rsrc(K + kv.kv_off, (uint32_t)N * kv.kvs * 2);
+  const auto rv = make_rsrc(V + kv.kv_off, (uint32_t)N * kv.kvs * 2);
+
+  bf16x8 kreg[KSTEPS], vreg[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    const uint32_t off = (uint32_t)key * (kv.kvs * 2) + (16 * kk + 8 * g) * 2;
+    kreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
+    vreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
+  }
+  f32x16 dk[DBLK], dv[DBLK];
+#pragma unroll
+  for (int bb = 0; bb < DBLK; ++bb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[bb][r] = 0.f;
+      dv[bb][r] = 0.f;
+    }
+
+  const int qstart = CAUSAL ? k0 : 0;
+  const int tph = (N - qstart + kTileRows - 1) / kTileRows;
+  const int ntiles = tph * group;
+  TileDma<D> dma;
+  dma.init(wave, lane, kv.qs);
+  TileReads<D> rd;
+  rd.init(lane);
+  auto qview = [&](int i) { return head_view(shape, b, hkv * group + i / tph, D); };
+  auto first_row = [&](int i) { return qstart + (i % tph) * kTileRows; };
+  // Tile i into a ring slot: Q and dO blocks, and 32 statistics per wave
+  // (wave w: rows 32(w & 1).. of LSE for w < 2, of D for w >= 2).
+  auto issue = [&](int i, bf16* qslot, bf16* dslot, float* sslot) {
+    const HeadView hq = qview(i);
+    const int r0 = first_row(i);
+    dma.issue(make_rsrc(Q + hq.q_off, (uint32_t)N * hq.qs * 2), qslot, r0, hq.qs);
+    dma.issue(make_rsrc(dO + hq.q_off, (uint32_t)N * hq.qs * 2), dslot, r0, hq.qs);
+    const auto rs = make_rsrc((wave < 2 ? LSE : delta) + hq.st_off, (uint32_t)N * 4);
+    if (lane < 8) lds_dma16(rs, sslot + 32 * wave, (uint32_t)(r0 + 32 * (wave & 1) + 4 * lane) * 4);
+  };
+  auto a_operand = [&](const bf16* qn, const bf16* dn, int m) {  // S/dP product m: block m/16, k-step (m%16)/2
+    return rd.row_major((m & 1) ? dn : qn, m / 16, (m % 16) / 2);
+  };
+  auto c_operand = [&](const bf16* qc, const bf16* dc, int m) {  // dV/dK product m: block m/16, d block (m%16)/4
+    return rd.transposed((m & 1) ? qc : dc, (m % 16) / 4, 2 * (m / 16) + (m % 4) / 2);
+  };
+  auto mask_tile = [&](int i, f32x16* s) {  // S -> -inf, dP -> 0 where the key is after the query or the row past N
+    const int q0 = first_row(i);
+    if (!((CAUSAL && q0 < kw + 31) || (q0 + kTileRows > N))) return;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qa = q0 + crow(qb, r, g);
+        const bool dead = qa >= N || (CAUSAL && key > qa);
+        s[2 * qb][r] = dead ? kNegInf : s[2 * qb][r];
+        s[2 * qb + 1][r] = dead ? 0.f : s[2 * qb + 1][r];
+      }
+  };
+
+  if (ntiles > 0) issue(0, qs0, ds0, ss0);
+  if (ntiles > 1) issue(1, qs1, ds1, ss1);
+  if (ntiles > 2) issue(2, qs2, ds2, ss2);
+  wait_vm_all();
+  __syncthreads();
+  if (first_row(0) + kTileRows > N) {
+    zero_rows<D>(qs0, N - first_row(0), tid);
+    zero_rows<D>(ds0, N - first_row(0), tid);
+    __syncthreads();
+  }
+  f32x16 sa[4], sb[4];  // [2 qb + (0: S, 1: dP)]
+  static_for<0, NA>([&](auto mc) __attribute__((always_inline)) {
+    constexpr int m = decltype(mc)::value;
+    const bf16x8 a = a_operand(qs0, ds0, m);
+    const bf16x8& bop = (m & 1) ? vreg[(m % 16) / 2] : kreg[(m % 16) / 2];
+    if constexpr ((m % 16) / 2 == 0)
+      mfma_s0(sa[2 * (m / 16) + (m & 1)], a, bop);
+    else
+      mfma_s(sa[2 * (m / 16) + (m & 1)], a, bop);
+  });
+  mfma_drain();
+
+  // kc/ds/sc: ring slot of tile t; kn/dn: of tile t+1; qd/dd/sd: the slot tile t+3 loads into (tile t-1's).
+  auto step = [&](int t, f32x16* sc, f32x16* sn, const bf16* qc, const bf16* dc, const float* stc, bf16* qn,
+                  bf16* dn, bf16* qd, bf16* dd, float* sd) {
+    if (t + 2 < ntiles)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VMEM_PER_TILE) : "memory");  // tile t+1 landed; t+2 may still fly
+    else
+      wait_vm_all();
+    __syncthreads();  // tile t+1 resident for every wave; tile t-1 consumed by every wave
+    if (t + 3 < ntiles) issue(t + 3, qd, dd, sd);
+    if (t + 1 < ntiles && first_row(t + 1) + kTileRows > N) {
+      zero_rows<D>(qn, N - first_row(t + 1), tid);
+      zero_rows<D>(dn, N - first_row(t + 1), tid);
+      __syncthreads();
+    }
+    mask_tile(t, sc);
+
+    bf16x8 op[LOOK + 1];
+    u32x4 pw[2][2], dw[2][2];  // P and dS of tile t as packed bf16 pairs: [query block][k-step]
+    float2 lse2[16], dl2[16];  // statistics of each value pair (read ahead)
+    static_for<0, LOOK>([&](auto ic) __attribute__((always_inline)) { op[ic.value] = a_operand(qn, dn, ic.value); });
+    // pair pi: query block pi/8, k-step (pi%8)/4, values 8h + 2w, +1 with w = pi % 4
+    constexpr int PH0 = 2, PSPAN = 44;
+    static_for<0, NT>([&](auto hc) __attribute__((always_inline)) {
+      constexpr int hs = decltype(hc)::value;
+      constexpr int ahead = hs + LOOK;
+      if constexpr (ahead < NA)
+        op[ahead % (LOOK + 1)] = a_operand(qn, dn, ahead);
+      else if constexpr (ahead < NT)
+        op[ahead % (LOOK + 1)] = c_operand(qc, dc, ahead - NA);
+      if constexpr (hs < NA) {
+        constexpr int m = hs;
+        const bf16x8& bop = (m & 1) ? vreg[(m % 16) / 2] : kreg[(m % 16) / 2];
+        if constexpr ((m % 16) / 2 == 0)
+          mfma_s0(sn[2 * (m / 16) + (m & 1)], op[hs % (LOOK + 1)], bop);
+        else
+          mfma_s(sn[2 * (m / 16) + (m & 1)], op[hs % (LOOK + 1)], bop);
+      } else {
+        constexpr int m = hs - NA;
+        constexpr int qb = m / 16, bb = (m % 16) / 4, h = (m % 4) / 2;
+        if constexpr (m & 1)
+          mfma_o(dk[bb], op[hs % (LOOK + 1)], __builtin_bit_cast(bf16x8, dw[qb][h]));
+        else
+          mfma_o(dv[bb], op[hs % (LOOK + 1)], __builtin_bit_cast(bf16x8, pw[qb][h]));
+      }
+      static_for<0, 16>([&](auto pc) __attribute__((always_inline)) {
+        constexpr int pi = decltype(pc)::value;
+        constexpr int qb = pi / 8, h = (pi % 8) / 4, w = pi % 4;
+        constexpr int at = PH0 + (pi * PSPAN) / 16;
+        if constexpr (at - 2 == hs) {  // statistics of the pair's two query rows
+          const int row = 32 * qb + 16 * h + 8 * g + 2 * w;
+          lse2[pi] = *reinterpret_cast<const float2*>(stc + row);
+          dl2[pi] = *reinterpret_cast<const float2*>(stc + kTileRows + row);
+        }
+        if constexpr (at == hs) {
+          constexpr int r = 8 * h + 2 * w;
+          const float p0 = exp2_fast(__builtin_fmaf(sc[2 * qb][r], scale_log2, -lse2[pi].x * kLog2e));
+          const float p1 = exp2_fast(__builtin_fmaf(sc[2 * qb][r + 1], scale_log2, -lse2[pi].y * kLog2e));
+          pw[qb][h][w] = pack_bf16x2(p0, p1);
+          dw[qb][h][w] = pack_bf16x2(p0 * (sc[2 * qb + 1][r] - dl2[pi].x), p1 * (sc[2 * qb + 1][r + 1] - dl2[pi].y));
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  for (int t = 0; t < ntiles; t += 4) {
+    step(t, sa, sb, qs0, ds0, ss0, qs1, ds1, qs3, ds3, ss3);
+    if (t + 1 < ntiles) step(t + 1, sb, sa, qs1, ds1, ss1, qs2, ds2, qs0, ds0, ss0);
+    if (t + 2 < ntiles) step(t + 2, sa, sb, qs2, ds2, ss2, qs3, ds3, qs1, ds1, ss1);
+    if (t + 3 < ntiles) step(t + 3, sb, sa, qs3, ds3, ss3, qs0, ds0, qs2, ds2, ss2);
+  }
+  mfma_drain();
+
+  // The key index is recomputed here (a lane count the compiler cannot hoist)
+  // rather than kept live across the loop.
+  int lane_e;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+  const int key_e = kw + (lane_e & 31);
+  if (kw >= N || key_e >= N) return;
+  bf16* dKrow = dK + kv.kv_off + (size_t)key_e * kv.kvs;
+  bf16* dVrow = dV + kv.kv_off + (size_t)key_e * kv.kvs;
+  // one accumulator block at a time out of the AGPRs
+  static_for<0, DBLK>([&](auto bc) __attribute__((always_inline)) {
+    constexpr int bb = decltype(bc)::value;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x2 wk, wv;
+      wk[0] = pack_bf16x2(dk[bb][4 * i] * scale, dk[bb][4 * i + 1] * scale);
+      wk[1] = pack_bf16x2(dk[bb][4 * i + 2] * scale, dk[bb][4 * i + 3] * scale);
+      wv[0] = pack_bf16x2(dv[bb][4 * i], dv[bb][4 * i + 1]);
+      wv[1] = pack_bf16x2(dv[bb][4 * i + 2], dv[bb][4 * i + 3]);
+      *reinterpret_cast<u32x2*>(dKrow + 32 * bb + 8 * i + 4 * g) = wk;
+      *reinterpret_cast<u32x2*>(dVrow + 32 * bb + 8 * i + 4 * g) = wv;
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
 // dQ: workgroup = 128 queries of one head; wavefront w owns qw..qw+31 and
 // walks their 64-key tiles (K and V tiles in an LDS ring).  Sᵀ and dPᵀ are
 // held as [key rows x this lane's query] as in the forward; Kᵀ for
@@ -480,15 +722,23 @@ hipError_t launch(const BackwardArgs& a) {
   const int tiles = (a.s.N + 127) / 128;
   const dim3 grid_kv((unsigned)(tiles * a.s.B * a.s.Hkv)), grid_q((unsigned)(tiles * a.s.B * a.s.H)), block(kThreads);
   if (a.causal) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), grid_kv, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
-                       static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.s, a.scale, sl2);
+    if (D == 128 && BWD_PIPE)
+      hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<true>), grid_kv, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
+                         static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.s, a.scale, sl2);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), grid_kv, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
+                         static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.s, a.scale, sl2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid_q, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
                        static_cast<bf16*>(a.dq), a.s, a.scale, sl2);
   } else {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), grid_kv, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
-                       static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.s, a.scale, sl2);
+    if (D == 128 && BWD_PIPE)
+      hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<false>), grid_kv, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
+                         static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.s, a.scale, sl2);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), grid_kv, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
+                         static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.s, a.scale, sl2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_kernel<D, false>), grid_q, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,

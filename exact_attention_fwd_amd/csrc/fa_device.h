@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef __bf16 bf16;
@@ -191,5 +193,42 @@ __device__ __forceinline__ HeadView kv_head_view(const Shape& s, int b, int hkv,
 // Key (or query) offset inside a 64-row tile of register r of C block kb, for
 // a lane in half g, when the A rows of the product were read via perm_row().
 __device__ __forceinline__ int crow(int kb, int r, int g) { return 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7); }
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Matrix products written as single instructions so that each operand sits
+// in the register file it is used from: blocks the VALU reads (scores) in
+// VGPRs; blocks only the matrix unit touches (output and gradient
+// accumulators, operands held for a whole pass) in AGPRs.  The compiler
+// cannot see the latency of these instructions: a VALU read of their results
+// that is not already separated by later pipeline slots is preceded by
+// mfma_drain().
+//   mfma_s0: s = a·b   mfma_s: s += a·b   (s in VGPRs, b in AGPRs)
+//   mfma_o:  o += a·p                     (o in AGPRs)
+__device__ __forceinline__ void mfma_s0(f32x16& s, const bf16x8& a, const bf16x8& q) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "a"(q));
+}
+__device__ __forceinline__ void mfma_s(f32x16& s, const bf16x8& a, const bf16x8& q) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "a"(q));
+}
+__device__ __forceinline__ void mfma_o(f32x16& o, const bf16x8& a, const bf16x8& p) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(p));
+}
+// x *= alpha for a value held in an accumulation register.
+__device__ __forceinline__ void acc_scale(float& x, float alpha) {
+  float t;
+  asm("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+      : "+a"(x), "=&v"(t)
+      : "v"(alpha));
+}
+// More wait states than a 32x32x16 product needs before its result is read.
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 }  // namespace fa

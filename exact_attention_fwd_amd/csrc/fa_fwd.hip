@@ -492,40 +492,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   if (LSE != nullptr && g == 0) LSE[hv.st_off + qrow] = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : kNegInf;
 }
 
-// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
-// Matrix products of the 64-query kernel, written as single instructions so
-// that each operand sits in the register file it is used from: score blocks
-// in VGPRs (the VALU reads them), the output accumulators and Qᵀ in AGPRs
-// (only the matrix unit touches them).  The compiler cannot see the latency
-// of these instructions: a VALU read of their results that is not already
-// separated by later slots is preceded by mfma_drain().
-__device__ __forceinline__ void mfma_s0(f32x16& s, const bf16x8& a, const bf16x8& q) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "a"(q));
-}
-__device__ __forceinline__ void mfma_s(f32x16& s, const bf16x8& a, const bf16x8& q) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "a"(q));
-}
-__device__ __forceinline__ void mfma_o(f32x16& o, const bf16x8& a, const bf16x8& p) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(p));
-}
-// x *= alpha for a value held in an accumulation register.
-__device__ __forceinline__ void acc_scale(float& x, float alpha) {
-  float t;
-  asm("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-      : "+a"(x), "=&v"(t)
-      : "v"(alpha));
-}
-// More wait states than a 32x32x16 product needs before its result is read.
-__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
-
 // The same forward with 64 queries per wavefront, for d = 128 with K/V laid
 // out like the queries (dense, grouped heads, packed batches): four
 // wavefronts per workgroup, one per SIMD.  Each K and Vᵀ operand read from
