@@ -29,9 +29,15 @@ METRIC = "attention TFLOP/s (fwd/bwd, % bf16 MFMA peak); paged-decode GB/s (% HB
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 KERNEL_SOURCES = {          # sources a kernel's counters depend on
-    "fwd_bf16_kernel": ["exact_attention_fwd_amd/csrc/fa_fwd.hip", "exact_attention_fwd_amd/csrc/fa_device.h"],
-    "decode_split_kernel": ["exact_attention_fwd_amd/csrc/fa_decode.hip"],
+    "fwd_w64_kernel": ["exact_attention_fwd_amd/csrc/fa_fwd.hip", "exact_attention_fwd_amd/csrc/fa_device.h"],
+    "decode_split_kernel": ["exact_attention_fwd_amd/csrc/fa_decode.hip", "exact_attention_fwd_amd/csrc/fa_device.h"],
 }
+
+
+def fwd_kernel_name(d, paged=False, rope=False):
+    """The forward kernel a launch runs: 64-query wavefronts for dense d = 128,
+    the 32-query kernel otherwise."""
+    return "fwd_w64_kernel" if (d == 128 and not paged and not rope) else "fwd_bf16_kernel"
 
 
 def pairs(N, causal):
@@ -112,7 +118,8 @@ def bench_forward(cfg, steps, warmup):
     avg, med, total = timed_launches(fn, steps, warmup)
     fl = fwd_flops(w.B, w.H, w.N, w.d, w.causal)
     del q, k, v, o, lse
-    return {"workload": w.name, "kernel": "fwd_bf16_kernel", "flops_per_launch": fl, "avg_ms": avg,
+    return {"workload": w.name, "kernel": fwd_kernel_name(w.d) if w.dtype == "bf16" else "fwd_f32_kernel",
+            "flops_per_launch": fl, "avg_ms": avg,
             "median_ms": med, "total_ms": total, "tflops": fl / (avg * 1e-3) / 1e12,
             "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
@@ -129,7 +136,7 @@ def bench_forward_gqa(steps, warmup, Hkv=8):
     fn = lambda: fa.forward(q, k, v, causal=True, scale=w.scale, out=o, lse=lse)
     avg, med, total = timed_launches(fn, steps, warmup)
     fl = fwd_flops(w.B, w.H, w.N, w.d, True)
-    return {"workload": f"fwd_gqa_causal_1x32q{Hkv}kv_16384x128", "kernel": "fwd_bf16_kernel",
+    return {"workload": f"fwd_gqa_causal_1x32q{Hkv}kv_16384x128", "kernel": fwd_kernel_name(128),
             "flops_per_launch": fl, "avg_ms": avg, "median_ms": med, "tflops": fl / (avg * 1e-3) / 1e12,
             "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
@@ -214,7 +221,7 @@ def bench_backward(steps, warmup):
     fn = lambda: fa.backward(q, k, v, o, do, lse, causal=w.causal, scale=w.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
     avg, med, total = timed_launches(fn, steps, warmup)
     fl = bwd_flops(w.B, w.H, w.N, w.d, w.causal)
-    return {"workload": w.name, "kernels": "bwd_delta + bwd_dkdv + bwd_dq", "flops_per_call": fl, "avg_ms": avg,
+    return {"workload": w.name, "kernels": "bwd_delta + bwd_dkdv_pipe + bwd_dq", "flops_per_call": fl, "avg_ms": avg,
             "median_ms": med, "tflops": fl / (avg * 1e-3) / 1e12,
             "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
@@ -359,8 +366,8 @@ def main():
         "config": {"workload": main_rec["workload"], "B": 1, "H": 32, "N": 16384, "d": 128, "causal": True,
                    "scale": 1 / math.sqrt(128)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for("fwd_bf16_kernel"),
-                     "kernel": "fwd_bf16_kernel", "avg_launch_ms": round(main_rec["avg_ms"], 4)},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(main_rec["kernel"]),
+                     "kernel": main_rec["kernel"], "avg_launch_ms": round(main_rec["avg_ms"], 4)},
         "cpu_baseline": base,
         "secondary": secondary,
     }
