@@ -34,26 +34,6 @@ constexpr int kThreads = 256;
 #define BWD_PIPE 1
 #endif
 
-// Linear block id -> (tile rank, batch entry, head).  Blocks go round-robin
-// over the 8 XCDs (XCD x runs the ids with id % 8 == x).  Units are numbered
-// head-major (u = h·B + b) and each XCD takes a contiguous range of them, so
-// a head's streamed tiles share that XCD's L2 and uneven sequence lengths of
-// a packed batch spread over all XCDs; rank 0 is dispatched first.
-__device__ __forceinline__ void map_unit(int bid, int B, int H, int& rank, int& b, int& h) {
-  const int BH = B * H;
-  int u;
-  if ((BH & 7) == 0) {
-    const int xcd = bid & 7, slot = bid >> 3, upx = BH >> 3;
-    rank = slot / upx;
-    u = xcd * upx + slot % upx;
-  } else {
-    rank = bid / BH;
-    u = bid % BH;
-  }
-  b = u % B;
-  h = u / B;
-}
-
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
@@ -186,7 +166,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
   int rank, b, hkv;
-  map_unit(blockIdx.x, shape.B, shape.Hkv, rank, b, hkv);
+  map_unit(blockIdx.x, shape.B, shape.Hkv, 1, rank, b, hkv);
   const int group = shape.H / shape.Hkv;  // query heads sharing this key/value head
   const HeadView kv = head_view(shape, b, hkv * group, D);
   const int N = kv.L;
@@ -387,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
   int rank, b, hkv;
-  map_unit(blockIdx.x, shape.B, shape.Hkv, rank, b, hkv);
+  map_unit(blockIdx.x, shape.B, shape.Hkv, 1, rank, b, hkv);
   const int group = shape.H / shape.Hkv;
   const HeadView kv = head_view(shape, b, hkv * group, D);
   const int N = kv.L;
@@ -595,7 +575,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
   int rank, bi, hi;
-  map_unit(blockIdx.x, shape.B, shape.H, rank, bi, hi);
+  map_unit(blockIdx.x, shape.B, shape.H, shape.H / shape.Hkv, rank, bi, hi);
   const HeadView hv = head_view(shape, bi, hi, D);
   const int N = hv.L;
   const int nqb = (N + 127) / 128;

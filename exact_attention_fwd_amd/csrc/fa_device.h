@@ -103,8 +103,16 @@ __device__ __forceinline__ int v_swz(int row) {
 // bounds branches.  (Word 3 = 0x00020000 is the CDNA data-format word for raw
 // 32-bit access.)
 // ---------------------------------------------------------------------------
+// Every descriptor in this library covers a range that is the same for the
+// whole wavefront; reading base and size through readfirstlane states that,
+// so the descriptor is built in scalar registers (a free move when they
+// already are) and loads through it never need a per-lane waterfall loop.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
@@ -193,6 +201,40 @@ __device__ __forceinline__ HeadView kv_head_view(const Shape& s, int b, int hkv,
 // Key (or query) offset inside a 64-row tile of register r of C block kb, for
 // a lane in half g, when the A rows of the product were read via perm_row().
 __device__ __forceinline__ int crow(int kb, int r, int g) { return 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7); }
+
+// Linear block id -> (tile rank, batch entry, head) for a grid of R tile
+// ranks per unit, units numbered head-major (u = h·B + b).  Blocks go
+// round-robin over the 8 XCDs (XCD x runs the ids with id % 8 == x) and
+// each XCD takes a contiguous range of units, so grouped heads (consecutive)
+// and whole heads of a batch share that XCD's L2.  With up to 32 units per
+// XCD the blocks go rank by rank across all of them: rank 0 (the caller's
+// heaviest tile) of every unit first.  With more units (many sequences of a
+// batch) they go in groups of G units, rank by rank within a group: G is
+// about 64 blocks' worth of units, so the concurrently running blocks stream
+// few units' key/value rows (L2 reuse) while each group still runs heaviest
+// first; with grouped heads (group > 1) G also covers the B·group units among
+// which every batch entry's query heads read the same key/value rows.
+__device__ __forceinline__ void map_unit(int bid, int B, int H, int group, int& rank, int& b, int& h) {
+  const int BH = B * H;
+  const bool split = (BH & 7) == 0;
+  const int upx = split ? BH >> 3 : BH;  // units per XCD
+  const int slot = split ? bid >> 3 : bid;
+  const int base = split ? (bid & 7) * upx : 0;
+  int u;
+  if (upx <= 32) {
+    rank = slot / upx;
+    u = base + slot % upx;
+  } else {
+    const int R = gridDim.x / BH;
+    const int G = min(upx, max((64 + R - 1) / R, group > 1 ? B * group : 1));
+    const int grp = slot / (G * R), idx = slot % (G * R);
+    const int gs = min(G, upx - grp * G);  // units in this group (the last may have fewer)
+    rank = idx / gs;
+    u = base + grp * G + idx % gs;
+  }
+  b = u % B;
+  h = u / B;
+}
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.
 template <int B, int E, typename F>

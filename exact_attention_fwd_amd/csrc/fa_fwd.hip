@@ -37,30 +37,6 @@ constexpr int kBC = 64;   // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 
-// Map the linear block id to (tile rank, batch entry, head).  Blocks are
-// handed out round-robin over the 8 XCDs, so the ids of one XCD are
-// bid % 8 == x.  Units are numbered head-major (u = h·B + b), and each XCD
-// takes a contiguous range of them: whole heads across every batch entry, so
-// uneven sequence lengths of a packed batch spread over all XCDs, and heads
-// that share key/value rows (grouped heads are consecutive) share an L2.
-// Within an XCD the tile ranks go in order; the caller turns rank 0 into the
-// heaviest tile of its own sequence.
-__device__ __forceinline__ void map_unit(int bid, int B, int H, int& rank, int& b, int& h) {
-  const int BH = B * H;
-  int u;
-  if ((BH & 7) == 0) {
-    const int xcd = bid & 7, slot = bid >> 3;
-    const int upx = BH >> 3;
-    rank = slot / upx;
-    u = xcd * upx + slot % upx;
-  } else {
-    rank = bid / BH;
-    u = bid % BH;
-  }
-  b = u % B;
-  h = u / B;
-}
-
 // m = max(m, a, b) as one v_max3_f32 that stays where it is written: work
 // scheduled into a pipeline slot must not be sunk out of it into the branch
 // that consumes it.
@@ -149,7 +125,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
   int rank, bi, hi;
-  map_unit(blockIdx.x, shape.B, shape.H, rank, bi, hi);
+  map_unit(blockIdx.x, shape.B, shape.H, shape.H / shape.Hkv, rank, bi, hi);
   const HeadView hv = head_view(shape, bi, hi, D);
   const int N = hv.L;  // this sequence's queries
   const int nqb = (N + kBR - 1) / kBR;
@@ -175,8 +151,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // Paged: key tile t (64 rows) is rows (t % 4)·64.. of pool page ptab[t / 4]; its
   // descriptor ends at the sequence's last key, so later slots are never fetched.
   auto page_rsrc = [&](int t, int half) {
+    // the page id is the same for every lane (one LDS address): keep the
+    // descriptor in scalar registers
+    const int page = __builtin_amdgcn_readfirstlane(ptab[t >> 2]);
     const bf16* base = static_cast<const bf16*>(pkv.pool) +
-                       ((size_t)ptab[t >> 2] * 2 * kPage + (size_t)half * kPage + (t & 3) * kTileRows) * kvs +
+                       ((size_t)page * 2 * kPage + (size_t)half * kPage + (t & 3) * kTileRows) * kvs +
                        (size_t)hkv * D;
     return make_rsrc(base, (uint32_t)min(kTileRows, Nk - t * kTileRows) * kvs * 2);
   };
@@ -521,7 +500,7 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
   int rank, bi, hi;
-  map_unit(blockIdx.x, shape.B, shape.H, rank, bi, hi);
+  map_unit(blockIdx.x, shape.B, shape.H, shape.H / shape.Hkv, rank, bi, hi);
   const HeadView hv = head_view(shape, bi, hi, D);
   const int N = hv.L;
   const int nqb = (N + kBR - 1) / kBR;
