@@ -568,7 +568,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   constexpr int DBLK = D / 32;
   constexpr int TILE = kTileRows * D;
   constexpr int BC = kTileRows;
-  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * 2 * TILE];  // [stage][K, V]
+  // two-stage ring [K tile | V tile], each stage its own LDS object named
+  // statically in the twice-unrolled loop: operand reads of one stage never
+  // wait on the loads still in flight into the other, and the V operand sits
+  // at a fixed offset from the K operand's address
+  __shared__ __attribute__((aligned(1024))) bf16 st0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 st1[2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -607,47 +612,50 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
   TileDma<D> dma;
   dma.init(wave, lane, hv.kvs);
-  TileReads<D> rd;
-  rd.init(lane);
+  TileReads<D> rd0;
+  rd0.init(lane);
 
   const int kv_end = CAUSAL ? min(N, q0 + 128) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
   const int wnt = (qw >= N) ? 0 : (CAUSAL ? min(ntiles, (min(qw + 31, N - 1) / BC) + 1) : ntiles);
-  auto issue = [&](int t) {
-    bf16* st = smem + (t & 1) * 2 * TILE;
-    dma.issue(rk, st, t * BC, hv.kvs);
-    dma.issue(rv, st + TILE, t * BC, hv.kvs);
+  auto issue = [&](int t, bf16* slot) {
+    dma.issue(rk, slot, t * BC, hv.kvs);
+    dma.issue(rv, slot + TILE, t * BC, hv.kvs);
   };
-  issue(0);
+  issue(0, st0);
 
-  for (int t = 0; t < ntiles; ++t) {
+  // Operand reads run LOOK products ahead of the product that consumes them
+  // (fenced slots keep that order): Sᵀ/dPᵀ products m = 0 .. 4·KSTEPS-1 read
+  // K or V rows, then the dQ products read Kᵀ transposed.
+  constexpr int LOOK = 2;
+  constexpr int NA = 4 * KSTEPS;   // Sᵀ and dPᵀ products
+  constexpr int NC = 4 * DBLK;     // dQᵀ products
+  auto step = [&](int t, bf16* kt, bf16* next) {
+    bf16* const vt = kt + TILE;
     const int k0 = t * BC;
     wait_vm_all();
     __syncthreads();  // tile t resident; tile t-1 consumed by every wave
-    if (t + 1 < ntiles) issue(t + 1);
-    bf16* kt = smem + (t & 1) * 2 * TILE;
-    bf16* vt = kt + TILE;
+    if (t + 1 < ntiles) issue(t + 1, next);
     if (k0 + BC > N) {  // tail: K rows past N must be zero for the transposed product
       zero_rows<D>(kt, N - k0, tid);
       __syncthreads();
     }
-    if (t >= wnt) continue;
+    if (t >= wnt) return;
 
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = mfma32(rd.row_major(kt, kb, 0), qreg[0], f32x16{});
-      dp[kb] = mfma32(rd.row_major(vt, kb, 0), oreg[0], f32x16{});
-#pragma unroll
-      for (int kk = 1; kk < KSTEPS; ++kk) {
-        s[kb] = mfma32(rd.row_major(kt, kb, kk), qreg[kk], s[kb]);
-        dp[kb] = mfma32(rd.row_major(vt, kb, kk), oreg[kk], dp[kb]);
-      }
-    }
+    // The lane offsets are re-derived per step (opaque copy) so that only one
+    // stage's LDS addresses are live at a time rather than both stages' sets.
+    TileReads<D> rd = rd0;
+    asm volatile("" : "+v"(rd.rmb), "+v"(rd.rmx), "+v"(rd.trd));
+    // product m < NA: key block m / (2 KSTEPS), k-step (m / 2) % KSTEPS, Sᵀ (even m) or dPᵀ (odd m)
+    auto a_op = [&](int m) { return rd.row_major((m & 1) ? vt : kt, m / (2 * KSTEPS), (m / 2) % KSTEPS); };
+    auto c_op = [&](int m) { return rd.transposed(kt, m % DBLK, m / DBLK); };  // dQ product m: chunk m / DBLK
     const bool need_mask = (CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > N) || (qw + 32 > N);
+    f32x16 s[2], dp[2];
     bf16x8 dsb[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    // dSᵀ for key block kb, right after its last product: the block's scores
+    // die before the next block's accumulate, which keeps two waves per SIMD
+    // in registers (the other wave's products cover this one's VALU work)
+    auto make_ds = [&](int kb) __attribute__((always_inline)) {
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -662,12 +670,39 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
       }
       dsb[2 * kb] = pack8(ds);
       dsb[2 * kb + 1] = pack8(ds + 8);
-    }
+    };
+    bf16x8 op[LOOK + 1];
+    static_for<0, LOOK>([&](auto ic) __attribute__((always_inline)) { op[ic.value] = a_op(ic.value); });
+    static_for<0, NA>([&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      constexpr int ahead = m + LOOK;
+      if constexpr (ahead < NA)
+        op[ahead % (LOOK + 1)] = a_op(ahead);
+      else
+        op[ahead % (LOOK + 1)] = c_op(ahead - NA);
+      __builtin_amdgcn_sched_barrier(0);  // the read goes out before this slot's product
+      constexpr int kb = m / (2 * KSTEPS), kk = (m / 2) % KSTEPS;
+      f32x16& acc = (m & 1) ? dp[kb] : s[kb];
+      acc = mfma32(op[m % (LOOK + 1)], (m & 1) ? oreg[kk] : qreg[kk], kk == 0 ? f32x16{} : acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (m % (2 * KSTEPS) == 2 * KSTEPS - 1) {
+        make_ds(kb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
     // dQᵀ += Kᵀ dSᵀ
-#pragma unroll
-    for (int b = 0; b < DBLK; ++b)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) dq[b] = mfma32(rd.transposed(kt, b, kk), dsb[kk], dq[b]);
+    static_for<0, NC>([&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      constexpr int ahead = NA + m + LOOK;
+      if constexpr (ahead < NA + NC) op[ahead % (LOOK + 1)] = c_op(ahead - NA);
+      __builtin_amdgcn_sched_barrier(0);
+      dq[m % DBLK] = mfma32(op[(NA + m) % (LOOK + 1)], dsb[m / DBLK], dq[m % DBLK]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, st0, st1);
+    if (t + 1 < ntiles) step(t + 1, st1, st0);
   }
 
   if (qw >= N || qrow >= N) return;
