@@ -630,6 +630,8 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
   constexpr int NT = NS + NP;
   constexpr int SPAN = NS + 3 * DBLK - 2;
   constexpr int MAX0 = NS + 2;
+  constexpr int MAXN = 2 * NT - 8;   // half-slots 2·MAX0 .. MAXN-1 take the max of S(t+1)
+  constexpr int DEC = 2 * NT - 6;    // half-slots DEC, DEC + 1: its reduction and rescale test
   auto tile_slots = [&](bool maskn, int t, f32x16* sc, f32x16* sn, const bf16* kn, const bf16* vs) {
     auto kread = [&](int i) {
       return *reinterpret_cast<const bf16x8*>(kn + (i / KSTEPS) * 32 * D + koff(i % KSTEPS));
@@ -646,6 +648,13 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
     bf16x8 op[LOOK + 1];
     u32x4 pw[2][4];  // P(t) of query block j, keys 16kk .. as packed bf16 pairs
     float mx[2] = {kNegInf, kNegInf};
+    float mt[2];
+    uint64_t need[2];
+    // max across the lane halves, scaled, and the lazy-rescale test
+    auto test = [&](int j) __attribute__((always_inline)) {
+      mt[j] = xhalf_max(mx[j]) * scale_log2;
+      need[j] = __builtin_amdgcn_ballot_w64(mt[j] > m_run[j] + kRescaleThreshold);
+    };
     static_for<0, LOOK>([&](auto ic) __attribute__((always_inline)) { op[ic.value] = kread(ic.value); });
     // Half-slots: one product each, so that with one wavefront per SIMD the
     // VALU work issues between consecutive products instead of waiting behind
@@ -685,11 +694,12 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
       });
       static_for<0, 32>([&](auto vc_) __attribute__((always_inline)) {
         constexpr int v = 2 * decltype(vc_)::value;  // values v, v+1 of S(t+1)
-        if constexpr (2 * MAX0 + (v * 2 * (NT - MAX0)) / 64 == hs) {
+        if constexpr (2 * MAX0 + (v * (MAXN - 2 * MAX0)) / 64 == hs) {
           constexpr int blk = v / 16;  // block 2kb + j
           max3_here(mx[blk % 2], sn[blk][v % 16], sn[blk][v % 16 + 1]);
         }
       });
+      if constexpr (hs == DEC || hs == DEC + 1) test(hs - DEC);
       __builtin_amdgcn_sched_barrier(0);
     });
 
@@ -703,14 +713,14 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx[j] = fmaxf(mx[j], sn[2 * kb + j][r]);
+          test(j);
         }
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const float m = xhalf_max(mx[j]) * scale_log2;
-        if (__builtin_amdgcn_ballot_w64(m > m_run[j] + kRescaleThreshold)) {
+        if (need[j]) {
           mfma_drain();
-          const float m_new = fmaxf(m_run[j], m);
+          const float m_new = fmaxf(m_run[j], mt[j]);
           const float alpha = exp2_fast(m_run[j] - m_new);
           l_run[j] *= alpha;
           // in place in the accumulation registers, one element at a time
