@@ -530,6 +530,22 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
     const int row = (wave * DMA_PER_WAVE + i) * ROWS_PER_DMA + dma_row;
     return (uint32_t)row * (kvs * 2) + ((dma_pc ^ (vtile ? v_swz<D>(row) : rm_swz<D>(row))) << 4);
   };
+  // Spread issue (one load at a time inside the slots): row r = 16·wave + 4i + dma_row,
+  // so the V chunk swizzle (a function of r % 4) is the same for every i and
+  // the K one is (dma_pc ^ dma_row) ^ (8(i & 1) + 4(i >> 1)); the row offset's
+  // i- and tile-dependent part is uniform.  `tbase` is the tile's byte offset,
+  // or an offset past every buffer for a load that is not needed (it then
+  // reads nothing and writes only a slot no one reads again).
+  const uint32_t drow = (uint32_t)(16 * wave + dma_row) * (uint32_t)(kvs * 2);
+  const uint32_t kch = (uint32_t)(dma_pc ^ dma_row) << 4;
+  const uint32_t vlane = drow + ((uint32_t)(dma_pc ^ v_swz<D>(dma_row)) << 4);
+  auto issue_k1 = [&](bf16* slot, uint32_t tbase, int i) {
+    const uint32_t ch = kch ^ ((uint32_t)(8 * (i & 1) + 4 * (i >> 1)) << 4);
+    lds_dma16(rk, slot + (wave * DMA_PER_WAVE + i) * 512, drow + ch + (tbase + (uint32_t)(4 * i * kvs * 2)));
+  };
+  auto issue_v1 = [&](bf16* slot, uint32_t tbase, int i) {
+    lds_dma16(rv, slot + (wave * DMA_PER_WAVE + i) * 512, vlane + (tbase + (uint32_t)(4 * i * kvs * 2)));
+  };
   auto issue_k = [&](bf16* slot, int t) {
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i)
@@ -632,7 +648,14 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
   constexpr int MAX0 = NS + 2;
   constexpr int MAXN = 2 * NT - 8;   // half-slots 2·MAX0 .. MAXN-1 take the max of S(t+1)
   constexpr int DEC = 2 * NT - 6;    // half-slots DEC, DEC + 1: its reduction and rescale test
-  auto tile_slots = [&](bool maskn, int t, f32x16* sc, f32x16* sn, const bf16* kn, const bf16* vs) {
+  // The loads of K(t+2) and V(t+1) go out one instruction every other
+  // half-slot from DMA0 on: issued in one burst, the four wavefronts' loads
+  // queue behind each other in the CU's memory pipeline and stall the issue.
+  constexpr int DMA0 = 1;
+  auto tile_slots = [&](bool maskn, int t, f32x16* sc, f32x16* sn, const bf16* kn, const bf16* vs,
+                        bf16* kdma, bf16* vdma) {
+    const uint32_t kt_base = t + 2 < ntiles ? (uint32_t)(t + 2) * (uint32_t)(64 * kvs * 2) : 0xF0000000u;
+    const uint32_t vt_base = t + 1 < ntiles ? (uint32_t)(t + 1) * (uint32_t)(64 * kvs * 2) : 0xF0000000u;
     auto kread = [&](int i) {
       return *reinterpret_cast<const bf16x8*>(kn + (i / KSTEPS) * 32 * D + koff(i % KSTEPS));
     };
@@ -700,6 +723,13 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
         }
       });
       if constexpr (hs == DEC || hs == DEC + 1) test(hs - DEC);
+      if constexpr (hs >= DMA0 && (hs - DMA0) % 2 == 0 && (hs - DMA0) / 2 < 2 * DMA_PER_WAVE) {
+        constexpr int i = (hs - DMA0) / 2;
+        if constexpr (i < DMA_PER_WAVE)
+          issue_k1(kdma, kt_base, i);
+        else
+          issue_v1(vdma, vt_base, i - DMA_PER_WAVE);
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
 
@@ -742,8 +772,6 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
     const int k0 = t * kBC;
     wait_vm_all();
     __syncthreads();  // K(t+1) and V(t) resident for every wave; tile t-1 fully consumed
-    if (t + 2 < ntiles) issue_k(kc, t + 2);
-    if (t + 1 < ntiles) issue_v(vn, t + 1);
     if (k0 + kBC > Nk) {  // tail tile: V rows past the last key must read as zero
       const int first = Nk - k0;
       for (int idx = tid; idx < (kBC - first) * CPR; idx += THREADS) {
@@ -752,9 +780,13 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
       }
       __syncthreads();
     }
-    if (t >= wnt) return;
+    if (t >= wnt) {  // nothing to compute here, but this wave's share of the loads still goes out
+      if (t + 2 < ntiles) issue_k(kc, t + 2);
+      if (t + 1 < ntiles) issue_v(vn, t + 1);
+      return;
+    }
     const int k0n = k0 + kBC;
-    tile_slots((CAUSAL && k0n + kBC - 1 > qw) || (k0n + kBC > Nk), t, sc, sn, kn, vc);
+    tile_slots((CAUSAL && k0n + kBC - 1 > qw) || (k0n + kBC > Nk), t, sc, sn, kn, vc, kc, vn);
   };
 
   for (int t = 0; t < ntiles; t += 2) {
