@@ -121,6 +121,17 @@ def test_batch_and_explicit_scale():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [300, 1000])
+def test_drifting_scores_forward(N, causal, d):
+    """Scores that grow along the key axis (about 8 rescales of the running
+    maximum per row over the sequence): the lazy-rescale path of the online
+    softmax, taken tile after tile, against the two-pass definition."""
+    q, k, v = workloads.drifting_inputs(1, 2, N, d, drift=4.0, seed=11 * N + d)
+    _fwd_compare(f"drift N={N} d={d} causal={causal}", q, k, v, causal, 1 / math.sqrt(d))
+
+
 def test_forward_is_deterministic_and_n0_is_noop():
     q, k, v = cuda(*workloads.attention_inputs(1, 8, 2000, 128, "bf16", seed=5))
     a = fa().forward(q, k, v, causal=True)

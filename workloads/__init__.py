@@ -86,6 +86,28 @@ def attention_inputs(B, H, N, d, dtype="bf16", seed=0, with_dout=False):
     return q, k, v, do
 
 
+def drifting_inputs(B, H, N, d, drift=4.0, seed=0):
+    """Q, K, V bf16 [B, H, N, d] whose scores grow along the key axis.
+
+    Every query and key shares a component along one random unit direction u:
+    q = z_q + sqrt(d)·u and k_j = z_k + drift·(j / N)·sqrt(d)·u with z ~ N(0, 1),
+    so q·k_j grows by about drift·d over the sequence.  A streaming pass then
+    meets a new, much larger row maximum tile after tile, which exercises the
+    rescaling of the partial output and normaliser (and the probability
+    underflow of early keys).
+    """
+    g = _gen(seed)
+    u = torch.randn(d, generator=g, dtype=torch.float32)
+    u = u / u.norm()
+    zq = torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
+    zk = torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
+    v = torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
+    ramp = drift * torch.arange(N, dtype=torch.float32) / max(N, 1)
+    q = zq + math.sqrt(d) * u
+    k = zk + (ramp[:, None] * math.sqrt(d)) * u
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
 @dataclass
 class PagedInputs:
     q: torch.Tensor            # [S, H, d] bf16
