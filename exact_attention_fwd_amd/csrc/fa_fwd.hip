@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
   int rank, bi, hi;
-  map_unit(blockIdx.x, shape.B, shape.H, shape.H / shape.Hkv, rank, bi, hi);
+  map_unit(blockIdx.x, shape.B, shape.H, shape.H / shape.Hkv, rank, bi, hi, true);
   const HeadView hv = head_view(shape, bi, hi, D);
   const int N = hv.L;  // this sequence's queries
   const int nqb = (N + kBR - 1) / kBR;
@@ -500,7 +500,7 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
   int rank, bi, hi;
-  map_unit(blockIdx.x, shape.B, shape.H, shape.H / shape.Hkv, rank, bi, hi);
+  map_unit(blockIdx.x, shape.B, shape.H, shape.H / shape.Hkv, rank, bi, hi, true);
   const HeadView hv = head_view(shape, bi, hi, D);
   const int N = hv.L;
   const int nqb = (N + kBR - 1) / kBR;
