@@ -44,9 +44,10 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 namespace fa {
 
+// Two fp32 per query row: D_i, then LSE_i · log2(e), each array rounded up to 256 bytes.
 size_t backward_workspace_bytes(long long rows) {
   if (rows < 0) return 0;
-  return round256((size_t)rows * sizeof(float));
+  return 2 * round256((size_t)rows * sizeof(float));
 }
 
 size_t decode_workspace_bytes(long long S, long long H, long long d, long long max_blocks) {
@@ -207,7 +208,9 @@ static fa_status backward_impl(fa_dtype dt, fa::AttnShape sh, int d, const void*
   if (!workspace || workspace_bytes < fa::backward_workspace_bytes(rows)) return FA_ERR_WORKSPACE;
   st = device_ready();
   if (st != FA_OK) return st;
-  fa::BackwardArgs a{sh, d, q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace), causal != 0, scale,
+  float* const ws = static_cast<float*>(workspace);
+  fa::BackwardArgs a{sh, d, q, k, v, o, dout, lse, dq, dk, dv, ws, ws + round256((size_t)rows * sizeof(float)) / sizeof(float),
+                     causal != 0, scale,
                      (hipStream_t)stream};
   return hip_status(fa::launch_backward(a));
 }

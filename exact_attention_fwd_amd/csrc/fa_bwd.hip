@@ -44,7 +44,8 @@ __device__ __forceinline__ float dpp(float x) {
 // (token j / H, head j % H) and D_i is stored [H, total] like the LSE.
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const bf16* __restrict__ O, const bf16* __restrict__ dO,
-                                                             float* __restrict__ delta, long long rows, int H,
+                                                             const float* __restrict__ LSE, float* __restrict__ delta,
+                                                             float* __restrict__ lse2, long long rows, int H,
                                                              long long total, int packed) {
   constexpr int LPR = D / 8;
   constexpr int RPB = kThreads / LPR;  // rows per block pass
@@ -64,7 +65,11 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const bf16* __restr
   acc += dpp<0x4E>(acc);
   acc += dpp<0x141>(acc);
   if (LPR == 16) acc += dpp<0x140>(acc);
-  if (row < rows && c == 0) delta[packed ? (row % H) * total + row / H : row] = acc;
+  if (row < rows && c == 0) {
+    const long long i = packed ? (row % H) * total + row / H : row;
+    delta[i] = acc;
+    lse2[i] = LSE[i] * kLog2e;  // the exponent base the tiles use
+  }
 }
 
 // Direct-to-LDS loads of a 64-row tile of a [rows, D] matrix (row-major in
@@ -338,8 +343,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 template <bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+    const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ delta,
     bf16* __restrict__ dK, bf16* __restrict__ dV, AttnShape shape, float scale, float scale_log2) {
+  // LSE2: the rows' logsumexp times log2(e), as the delta kernel writes it
   constexpr int D = 128;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
@@ -356,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 ds1[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 ds2[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 ds3[TILE];
-  // statistics of a tile: LSE of its 64 query rows, then D of those rows
+  // statistics of a tile: LSE · log2(e) of its 64 query rows, then D of those rows
   __shared__ __attribute__((aligned(16))) float ss0[2 * kTileRows];
   __shared__ __attribute__((aligned(16))) float ss1[2 * kTileRows];
   __shared__ __attribute__((aligned(16))) float ss2[2 * kTileRows];
@@ -410,7 +416,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
     const int r0 = first_row(i);
     dma.issue(make_rsrc(Q + hq.q_off, (uint32_t)N * hq.qs * 2), qslot, r0, hq.qs);
     dma.issue(make_rsrc(dO + hq.q_off, (uint32_t)N * hq.qs * 2), dslot, r0, hq.qs);
-    const auto rs = make_rsrc((wave < 2 ? LSE : delta) + hq.st_off, (uint32_t)N * 4);
+    const auto rs = make_rsrc((wave < 2 ? LSE2 : delta) + hq.st_off, (uint32_t)N * 4);
     if (lane < 8) lds_dma16(rs, sslot + 32 * wave, (uint32_t)(r0 + 32 * (wave & 1) + 4 * lane) * 4);
   };
   auto a_operand = [&](const bf16* qn, const bf16* dn, int m) {  // S/dP product m: block m/16, k-step (m%16)/2
@@ -510,8 +516,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
         }
         if constexpr (at == hs) {
           constexpr int r = 8 * h + 2 * w;
-          const float p0 = exp2_fast(__builtin_fmaf(sc[2 * qb][r], scale_log2, -lse2[pi].x * kLog2e));
-          const float p1 = exp2_fast(__builtin_fmaf(sc[2 * qb][r + 1], scale_log2, -lse2[pi].y * kLog2e));
+          const float p0 = exp2_fast(__builtin_fmaf(sc[2 * qb][r], scale_log2, -lse2[pi].x));
+          const float p1 = exp2_fast(__builtin_fmaf(sc[2 * qb][r + 1], scale_log2, -lse2[pi].y));
           pw[qb][h][w] = pack_bf16x2(p0, p1);
           dw[qb][h][w] = pack_bf16x2(p0 * (sc[2 * qb + 1][r] - dl2[pi].x), p1 * (sc[2 * qb + 1][r + 1] - dl2[pi].y));
         }
@@ -725,7 +731,7 @@ hipError_t launch(const BackwardArgs& a) {
   constexpr int RPB = kThreads / (D / 8);
   if (rows > 0)
     hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kThreads), 0, a.stream,
-                       static_cast<const bf16*>(a.o), static_cast<const bf16*>(a.dout), a.delta, rows, a.s.H,
+                       static_cast<const bf16*>(a.o), static_cast<const bf16*>(a.dout), a.lse, a.delta, a.lse2, rows, a.s.H,
                        (long long)a.s.total, packed ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -738,7 +744,7 @@ hipError_t launch(const BackwardArgs& a) {
   const dim3 grid_kv((unsigned)(tiles * a.s.B * a.s.Hkv)), grid_q((unsigned)(tiles * a.s.B * a.s.H)), block(kThreads);
   if (a.causal) {
     if (D == 128 && BWD_PIPE)
-      hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<true>), grid_kv, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
+      hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<true>), grid_kv, block, 0, a.stream, q, k, v, dout, a.lse2, a.delta,
                          static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.s, a.scale, sl2);
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), grid_kv, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
@@ -749,7 +755,7 @@ hipError_t launch(const BackwardArgs& a) {
                        static_cast<bf16*>(a.dq), a.s, a.scale, sl2);
   } else {
     if (D == 128 && BWD_PIPE)
-      hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<false>), grid_kv, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
+      hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<false>), grid_kv, block, 0, a.stream, q, k, v, dout, a.lse2, a.delta,
                          static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.s, a.scale, sl2);
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), grid_kv, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,

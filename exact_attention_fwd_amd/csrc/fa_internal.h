@@ -72,6 +72,7 @@ struct BackwardArgs {
   void* dk;
   void* dv;
   float* delta;  // D_i, laid out like LSE (workspace)
+  float* lse2;   // LSE_i · log2(e), laid out like LSE (workspace)
   int causal;
   float scale;
   hipStream_t stream;

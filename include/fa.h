@@ -91,8 +91,9 @@ fa_status fa_forward(fa_dtype dt, int B, int H, int N, int d,
                      void* o, float* lse, int causal, float scale, void* stream);
 
 /*
- * Workspace the backward needs, in bytes: one fp32 per query row (the row
- * dot product D_i = dO_i · O_i), rounded up to 256 bytes.  O(B·H·N); no N×N.
+ * Workspace the backward needs, in bytes: two fp32 per query row (the row
+ * dot product D_i = dO_i · O_i, and the row's logsumexp in base-2 units), each
+ * array rounded up to 256 bytes.  O(B·H·N); no N×N.
  */
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
 

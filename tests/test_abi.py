@@ -55,12 +55,12 @@ def test_status_strings_and_version(L):
 
 
 def test_workspace_sizes(L):
-    assert L.fa_backward_workspace_bytes(2, 16, 8192, 128) == 2 * 16 * 8192 * 4
-    assert L.fa_backward_workspace_bytes(1, 1, 7, 64) == 256
+    assert L.fa_backward_workspace_bytes(2, 16, 8192, 128) == 2 * (2 * 16 * 8192 * 4)
+    assert L.fa_backward_workspace_bytes(1, 1, 7, 64) == 2 * 256
     assert L.fa_backward_workspace_bytes(0, 1, 7, 64) == 0
     assert L.fa_decode_workspace_bytes(8, 32, 128, 32) == 8 * 32 * 32 * 2 * 130 * 4
     # linear in N: no N x N buffer anywhere
-    assert L.fa_backward_workspace_bytes(1, 1, 32768, 128) == 32768 * 4
+    assert L.fa_backward_workspace_bytes(1, 1, 32768, 128) == 2 * 32768 * 4
 
 
 def fwd(L, dt=1, B=1, H=1, N=16, d=128, ptr=FAKE, lse=FAKE, causal=0, scale=0.1):
