@@ -207,7 +207,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   TileReads<D> rd;
   rd.init(lane);
   // Query-side addressing of tile i: query head hkv*group + i / tph, rows from qstart + (i % tph)*64.
-  auto qview = [&](int i) { return head_view(shape, b, hkv * group + i / tph, D); };
+  // (Offsets stepped from the first query head's view: recomputing the view would
+  // re-read the packed layout's sequence offsets from memory at every tile.)
+  auto qview = [&](int i) { return step_head(kv, shape, i / tph, D); };
   auto issue = [&](int i) {
     const HeadView hq = qview(i);
     bf16* st = smem + (i & 1) * 2 * TILE;
@@ -407,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
   dma.init(wave, lane, kv.qs);
   TileReads<D> rd;
   rd.init(lane);
-  auto qview = [&](int i) { return head_view(shape, b, hkv * group + i / tph, D); };
+  auto qview = [&](int i) { return step_head(kv, shape, i / tph, D); };  // as in the kernel above
   auto first_row = [&](int i) { return qstart + (i % tph) * kTileRows; };
   // Tile i into a ring slot: Q and dO blocks, and 32 statistics per wave
   // (wave w: rows 32(w & 1).. of LSE for w < 2, of D for w >= 2).
@@ -469,7 +471,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
     else
       wait_vm_all();
     __syncthreads();  // tile t+1 resident for every wave; tile t-1 consumed by every wave
-    if (t + 3 < ntiles) issue(t + 3, qd, dd, sd);
+    // Tile t+3's loads go out one every other half-slot (below) rather than in
+    // a burst here, where the four wavefronts' bursts queue behind each other in
+    // the CU's memory pipeline.  Past the last tile they aim beyond the
+    // buffers and fetch nothing, so every step issues the same number of loads.
+    const int i3 = min(t + 3, ntiles - 1);
+    const uint32_t bias = t + 3 < ntiles ? 0u : 0xF0000000u;
+    const HeadView hq3 = qview(i3);
+    const int r03 = first_row(i3);
+    const auto rq3 = make_rsrc(Q + hq3.q_off, (uint32_t)N * hq3.qs * 2);
+    const auto rd3 = make_rsrc(dO + hq3.q_off, (uint32_t)N * hq3.qs * 2);
+    const auto rs3 = make_rsrc((wave < 2 ? LSE2 : delta) + hq3.st_off, (uint32_t)N * 4);
+    const uint32_t roff = (uint32_t)r03 * (uint32_t)(hq3.qs * 2) + bias;
     if (t + 1 < ntiles && first_row(t + 1) + kTileRows > N) {
       zero_rows<D>(qn, N - first_row(t + 1), tid);
       zero_rows<D>(dn, N - first_row(t + 1), tid);
@@ -490,6 +503,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
         op[ahead % (LOOK + 1)] = a_operand(qn, dn, ahead);
       else if constexpr (ahead < NT)
         op[ahead % (LOOK + 1)] = c_operand(qc, dc, ahead - NA);
+      if constexpr (hs % 2 == 1 && hs / 2 <= 2 * TileDma<D>::DPW) {
+        constexpr int i = hs / 2;
+        if constexpr (i < TileDma<D>::DPW)
+          lds_dma16(rq3, qd + (dma.base_blk + i) * 512, dma.off[i] + roff);
+        else if constexpr (i < 2 * TileDma<D>::DPW)
+          lds_dma16(rd3, dd + (dma.base_blk + i - TileDma<D>::DPW) * 512, dma.off[i - TileDma<D>::DPW] + roff);
+        else if (lane < 8)
+          lds_dma16(rs3, sd + 32 * wave, (uint32_t)(r03 + 32 * (wave & 1) + 4 * lane) * 4 + bias);
+      }
       if constexpr (hs < NA) {
         constexpr int m = hs;
         const bf16x8& bop = (m & 1) ? vreg[(m % 16) / 2] : kreg[(m % 16) / 2];

@@ -191,6 +191,19 @@ __device__ __forceinline__ HeadView head_view(const Shape& s, int b, int h, int 
   }
   return v;
 }
+// The view of query head h + j of the same batch entry, from the view of head
+// h (query-side offsets only; the key/value fields are left as they are).
+template <typename Shape>
+__device__ __forceinline__ HeadView step_head(HeadView v, const Shape& s, int j, int D) {
+  if (s.cu == nullptr) {
+    v.q_off += (size_t)j * s.N * D;
+    v.st_off += (size_t)j * s.N;
+  } else {
+    v.q_off += (size_t)j * D;
+    v.st_off += (size_t)j * s.total;
+  }
+  return v;
+}
 // Same addressing for a (batch, key/value head) unit (its K/V rows only).
 template <typename Shape>
 __device__ __forceinline__ HeadView kv_head_view(const Shape& s, int b, int hkv, int D) {
