@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const bf16* __restr
   if (LPR == 16) acc += dpp<0x140>(acc);
   if (row < rows && c == 0) {
     const long long i = packed ? (row % H) * total + row / H : row;
-    delta[i] = acc;
+    delta[i] = -acc;            // −D_i: a dP accumulator can start from it
     lse2[i] = LSE[i] * kLog2e;  // the exponent base the tiles use
   }
 }
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       for (int r = 0; r < 16; ++r) {
         const int qi = crow(qb, r, g);
         float pr = exp2_fast(__builtin_fmaf(sv[r], scale_log2, -lse2[qi]));
-        float dsr = pr * (dpv[r] - dlt[qi]);
+        float dsr = pr * (dpv[r] + dlt[qi]);  // dlt holds −D
         if constexpr (decltype(masked)::value) {
           const int qa = q0 + qi;
           const bool dead = qa >= N || key >= N || (CAUSAL && key > qa);
@@ -441,6 +441,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
       }
   };
 
+  // dP accumulators of query block qb start at −D of their rows (register r:
+  // row 32qb + 16(r / 8) + 8g + r % 8 of the tile's statistics), so the products
+  // accumulate dP − D and dS = P ∘ (dP − D) takes one multiply per score.
+  auto d_init = [&](f32x16& acc, const float* st, int qb) {
+#pragma unroll
+    for (int run = 0; run < 2; ++run) {
+      const float4 x0 = *reinterpret_cast<const float4*>(st + kTileRows + 32 * qb + 16 * run + 8 * g);
+      const float4 x1 = *reinterpret_cast<const float4*>(st + kTileRows + 32 * qb + 16 * run + 8 * g + 4);
+      acc[8 * run + 0] = x0.x; acc[8 * run + 1] = x0.y; acc[8 * run + 2] = x0.z; acc[8 * run + 3] = x0.w;
+      acc[8 * run + 4] = x1.x; acc[8 * run + 5] = x1.y; acc[8 * run + 6] = x1.z; acc[8 * run + 7] = x1.w;
+    }
+  };
+
   if (ntiles > 0) issue(0, qs0, ds0, ss0);
   if (ntiles > 1) issue(1, qs1, ds1, ss1);
   if (ntiles > 2) issue(2, qs2, ds2, ss2);
@@ -451,12 +464,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
     zero_rows<D>(ds0, N - first_row(0), tid);
     __syncthreads();
   }
-  f32x16 sa[4], sb[4];  // [2 qb + (0: S, 1: dP)]
+  f32x16 sa[4], sb[4];  // [2 qb + (0: S, 1: dP − D)]
+  d_init(sa[1], ss0, 0);
+  d_init(sa[3], ss0, 1);
   static_for<0, NA>([&](auto mc) __attribute__((always_inline)) {
     constexpr int m = decltype(mc)::value;
     const bf16x8 a = a_operand(qs0, ds0, m);
     const bf16x8& bop = (m & 1) ? vreg[(m % 16) / 2] : kreg[(m % 16) / 2];
-    if constexpr ((m % 16) / 2 == 0)
+    if constexpr ((m % 16) / 2 == 0 && (m & 1) == 0)
       mfma_s0(sa[2 * (m / 16) + (m & 1)], a, bop);
     else
       mfma_s(sa[2 * (m / 16) + (m & 1)], a, bop);
@@ -465,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
 
   // kc/ds/sc: ring slot of tile t; kn/dn: of tile t+1; qd/dd/sd: the slot tile t+3 loads into (tile t-1's).
   auto step = [&](int t, f32x16* sc, f32x16* sn, const bf16* qc, const bf16* dc, const float* stc, bf16* qn,
-                  bf16* dn, bf16* qd, bf16* dd, float* sd) {
+                  bf16* dn, const float* stn, bf16* qd, bf16* dd, float* sd) {
     if (t + 2 < ntiles)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VMEM_PER_TILE) : "memory");  // tile t+1 landed; t+2 may still fly
     else
@@ -492,7 +507,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
 
     bf16x8 op[LOOK + 1];
     u32x4 pw[2][2], dw[2][2];  // P and dS of tile t as packed bf16 pairs: [query block][k-step]
-    float2 lse2[16], dl2[16];  // statistics of each value pair (read ahead)
+    float2 lse2[16];  // statistics of each value pair (read ahead)
+    d_init(sn[1], stn, 0);
     static_for<0, LOOK>([&](auto ic) __attribute__((always_inline)) { op[ic.value] = a_operand(qn, dn, ic.value); });
     // pair pi: query block pi/8, k-step (pi%8)/4, values 8h + 2w, +1 with w = pi % 4
     constexpr int PH0 = 2, PSPAN = 44;
@@ -512,10 +528,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
         else if (lane < 8)
           lds_dma16(rs3, sd + 32 * wave, (uint32_t)(r03 + 32 * (wave & 1) + 4 * lane) * 4 + bias);
       }
+      if constexpr (hs == 12) d_init(sn[3], stn, 1);  // ahead of block 1's first dP product
       if constexpr (hs < NA) {
         constexpr int m = hs;
         const bf16x8& bop = (m & 1) ? vreg[(m % 16) / 2] : kreg[(m % 16) / 2];
-        if constexpr ((m % 16) / 2 == 0)
+        if constexpr ((m % 16) / 2 == 0 && (m & 1) == 0)
           mfma_s0(sn[2 * (m / 16) + (m & 1)], op[hs % (LOOK + 1)], bop);
         else
           mfma_s(sn[2 * (m / 16) + (m & 1)], op[hs % (LOOK + 1)], bop);
@@ -534,14 +551,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
         if constexpr (at - 2 == hs) {  // statistics of the pair's two query rows
           const int row = 32 * qb + 16 * h + 8 * g + 2 * w;
           lse2[pi] = *reinterpret_cast<const float2*>(stc + row);
-          dl2[pi] = *reinterpret_cast<const float2*>(stc + kTileRows + row);
         }
         if constexpr (at == hs) {
           constexpr int r = 8 * h + 2 * w;
           const float p0 = exp2_fast(__builtin_fmaf(sc[2 * qb][r], scale_log2, -lse2[pi].x));
           const float p1 = exp2_fast(__builtin_fmaf(sc[2 * qb][r + 1], scale_log2, -lse2[pi].y));
           pw[qb][h][w] = pack_bf16x2(p0, p1);
-          dw[qb][h][w] = pack_bf16x2(p0 * (sc[2 * qb + 1][r] - dl2[pi].x), p1 * (sc[2 * qb + 1][r + 1] - dl2[pi].y));
+          dw[qb][h][w] = pack_bf16x2(p0 * sc[2 * qb + 1][r], p1 * sc[2 * qb + 1][r + 1]);
         }
       });
       __builtin_amdgcn_sched_barrier(0);
@@ -549,10 +565,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
   };
 
   for (int t = 0; t < ntiles; t += 4) {
-    step(t, sa, sb, qs0, ds0, ss0, qs1, ds1, qs3, ds3, ss3);
-    if (t + 1 < ntiles) step(t + 1, sb, sa, qs1, ds1, ss1, qs2, ds2, qs0, ds0, ss0);
-    if (t + 2 < ntiles) step(t + 2, sa, sb, qs2, ds2, ss2, qs3, ds3, qs1, ds1, ss1);
-    if (t + 3 < ntiles) step(t + 3, sb, sa, qs3, ds3, ss3, qs0, ds0, qs2, ds2, ss2);
+    step(t, sa, sb, qs0, ds0, ss0, qs1, ds1, ss1, qs3, ds3, ss3);
+    if (t + 1 < ntiles) step(t + 1, sb, sa, qs1, ds1, ss1, qs2, ds2, ss2, qs0, ds0, ss0);
+    if (t + 2 < ntiles) step(t + 2, sa, sb, qs2, ds2, ss2, qs3, ds3, ss3, qs1, ds1, ss1);
+    if (t + 3 < ntiles) step(t + 3, sb, sa, qs3, ds3, ss3, qs0, ds0, ss0, qs2, ds2, ss2);
   }
   mfma_drain();
 
@@ -630,7 +646,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     oreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
   }
   const float lse2 = (qrow < N) ? LSE[hv.st_off + qrow] * kLog2e : 0.f;
-  const float dl = (qrow < N) ? delta[hv.st_off + qrow] : 0.f;
+  const float dl = (qrow < N) ? delta[hv.st_off + qrow] : 0.f;  // −D of this row
 
   f32x16 dq[DBLK];
 #pragma unroll
@@ -688,7 +704,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pr = exp2_fast(__builtin_fmaf(s[kb][r], scale_log2, -lse2));
-        float dsr = pr * (dp[kb][r] - dl);
+        float dsr = pr * (dp[kb][r] + dl);
         if (need_mask) {
           const int ka = k0 + crow(kb, r, g);
           const bool dead = ka >= N || qrow >= N || (CAUSAL && ka > qrow);

@@ -71,7 +71,7 @@ struct BackwardArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // D_i, laid out like LSE (workspace)
+  float* delta;  // −D_i, laid out like LSE (workspace)
   float* lse2;   // LSE_i · log2(e), laid out like LSE (workspace)
   int causal;
   float scale;
