@@ -16,14 +16,18 @@
 // running max, normaliser and unnormalised output.
 // Kernel 1' (split, grouped key/value heads): the g = H / Hkv query heads
 // that share a key/value head read each K/V row once.  Each wavefront works
-// alone on one (sequence, half page, key/value head, block of up to 32 of its
-// query heads) and streams the half page in 32-token tiles: while tile t is
-// computed, tile t+1's K rows load into registers and its V rows into the
-// wave's LDS ring.  Sᵀ = K·Qᵀ runs on bf16 MFMA with the group's queries as
-// the 32 columns and K read straight into operand registers (16 contiguous
-// bytes of a token row per lane); the per-head online softmax is then a
-// column reduction inside a lane pair, and Oᵀ += Vᵀ·Pᵀ reads Vᵀ transposed out
-// of the ring.  One partial per (sequence, query head, half page).
+// alone on one (sequence, split, key/value head, block of up to 32 of its
+// query heads), the split being a whole page when the block table is large
+// enough to fill the chip that way and half a page otherwise, and streams
+// the split in 32-token tiles.  Tile loads read
+// whole token rows (16 lanes per 256-byte row, so every cache line fetched
+// is used by one instruction) into staging registers; at the start of a tile
+// they move to the wave's own K and V tiles in LDS and the registers take the
+// next tile's loads.  Sᵀ = K·Qᵀ runs on bf16 MFMA with the group's queries as
+// the 32 columns and K rows read back from LDS in operand layout; the
+// per-head online softmax is then a column reduction inside a lane pair, and
+// Oᵀ += Vᵀ·Pᵀ reads Vᵀ transposed out of LDS.  One partial per (sequence,
+// query head, split).
 // Multi-query / grouped-query sharing of K/V is the adaptation named by
 // "Flash Attention 是什么" (ai.lansai.wang), 进阶学习路径 §4.
 // Kernel 2 (merge): combines the partials of a (sequence, head) exactly:
@@ -206,29 +210,41 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 
 // Query heads per wavefront of the grouped kernel (the MFMA's 32 columns).
 constexpr int kGqaCols = 32;
-constexpr int kGqaTokens = 128;  // tokens per wavefront (two partials per page)
+// Tokens per wavefront: a whole page when the grid is large enough to fill
+// the chip with pages (fewer partials to merge, longer streams per
+// wavefront), half a page otherwise.
+constexpr int kGqaPageUnits = 1024;
 constexpr int kGqaTile = 32;     // tokens per streamed tile
 
-// Wait until at most N vector-memory operations of this wavefront are in flight.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+// Swizzle of the K tile in LDS: 16-byte chunk c of tile row r sits at
+// position c ^ k_swz(r).  The rows are read back as an MFMA operand, lane n
+// (of 32) taking row perm_row(n), so the swizzle is a function of n: with
+// d = 128 (16 chunks per 256-byte row) the 16 lanes of a read hit 16
+// distinct chunk positions, with d = 64 (two rows per 256 bytes) the pairs
+// (row parity, position) are distinct; in both cases every 8 consecutive
+// lanes also differ modulo 128 bytes.  Writes (16 lanes along one row) are
+// free of conflicts for any swizzle.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  const int n = perm_row(row);
+  return D >= 128 ? (n & 15) : ((n & 7) ^ ((n >> 3) & 1));
 }
 
-template <int D>
+template <int D, int TPW>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_gqa_split_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ pool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part, int S, int H, int Hkv, int num_pages,
     int max_blocks, float scale_log2) {
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
-  constexpr int CPR = D / 8;                    // 16-byte chunks per row
-  constexpr int ROWS_PER_DMA = 64 / CPR;        // rows per 1 KiB wavefront load
-  constexpr int NDMA = kGqaTile / ROWS_PER_DMA; // loads per V tile
-  constexpr int VT = kGqaTile * D;              // bf16 elements of one V tile
-  constexpr int SPP = kPage / kGqaTokens;       // partials per page
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int RPL = 64 / CPR;               // rows per wavefront load (one row per CPR lanes)
+  constexpr int NLD = kGqaTile / RPL;         // loads per tile, for K and for V
+  constexpr int VT = kGqaTile * D;            // bf16 elements of one tile
+  constexpr int SPP = kPage / TPW;            // partials per page
   constexpr int kWaves = kDecThreads / 64;
-  __shared__ __attribute__((aligned(1024))) bf16 vring[kWaves][2][VT];
+  __shared__ __attribute__((aligned(1024))) bf16 ktile[kWaves][VT];
+  __shared__ __attribute__((aligned(1024))) bf16 vtile[kWaves][VT];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -248,10 +264,15 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_gqa_split_kernel(
   const int s = (int)(unit / nsplit);
   if (s >= S) return;  // padding of the last workgroup
   const int b = sp / SPP;                      // logical page
-  const int t0 = (sp % SPP) * kGqaTokens;      // first slot of this split in the page
-  const int ntok = min(kGqaTokens, seq_lens[s] - b * kPage - t0);
+  const int t0 = (sp % SPP) * TPW;             // first slot of this split in the page
+  // Both loads issue before the exit test (one memory latency, not two): the
+  // empty asm consumes the table entry there, so it cannot sink below the test.
+  const int len = seq_lens[s];
+  const int entry = block_table[(size_t)s * max_blocks + b];
+  asm volatile("" ::"s"(entry));
+  const int ntok = min(TPW, len - b * kPage - t0);
   if (ntok <= 0) return;  // split past the sequence end
-  const int page = min(max(block_table[(size_t)s * max_blocks + b], 0), num_pages - 1);
+  const int page = min(max(entry, 0), num_pages - 1);
   const int cols = min(kGqaCols, group - hb * kGqaCols);  // query heads of this block
   const int hq0 = hkv * group + hb * kGqaCols;             // its first query head
 
@@ -261,21 +282,35 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_gqa_split_kernel(
   const bf16* kbase = pool + (size_t)page * 2 * kPage * Hkv * D + (size_t)t0 * Hkv * D + (size_t)hkv * D;
   const auto rk = make_rsrc(kbase, (uint32_t)ntok * tok_bytes);
   const auto rv = make_rsrc(kbase + (size_t)kPage * Hkv * D, (uint32_t)ntok * tok_bytes);
-  bf16* ring = &vring[wave][0][0];
-  const int dma_row = lane / CPR, dma_pc = lane % CPR;
-  // Tile t: K rows 32t + perm_row(n) into operand registers, V rows 32t.. into ring slot t & 1.
-  auto issue = [&](int t, bf16x8* kr) {
+  bf16* kt = &ktile[wave][0];
+  bf16* vt = &vtile[wave][0];
+  // Tile loads read whole rows: CPR lanes cover one token's D features, so
+  // each load instruction fetches RPL complete rows.
+  const int ld_row = lane / CPR, ld_c = lane % CPR;
+  const uint32_t ld_off = (uint32_t)ld_row * tok_bytes + 16u * ld_c;
+  u32x4 kst[NLD], vst[NLD];
+  auto load = [&](int t) {  // tile t into the staging registers (rows past ntok: zeros, no fetch)
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk)
-      kr[kk] = __builtin_bit_cast(
-          bf16x8, buf_load16_stream(rk, (uint32_t)(kGqaTile * t + perm_row(n)) * tok_bytes + (16 * kk + 8 * g) * 2));
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const int row = i * ROWS_PER_DMA + dma_row;
-      lds_dma16(rv, ring + (t & 1) * VT + i * 512,
-                (uint32_t)(kGqaTile * t + row) * tok_bytes + ((dma_pc ^ v_swz<D>(row)) << 4));
+    for (int i = 0; i < NLD; ++i) {
+      const uint32_t off = (uint32_t)(kGqaTile * t + RPL * i) * tok_bytes + ld_off;
+      kst[i] = buf_load16_stream(rk, off);
+      vst[i] = buf_load16_stream(rv, off);
     }
   };
+  // Staging registers -> LDS: K row r, chunk c at c ^ k_swz(r) (read back as
+  // operand rows), V at c ^ v_swz(r) (read back transposed).
+  int kw_off[NLD], vw_off[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int row = RPL * i + ld_row;
+    kw_off[i] = row * D + ((ld_c ^ k_swz<D>(row)) << 3);
+    vw_off[i] = row * D + ((ld_c ^ v_swz<D>(row)) << 3);
+  }
+  load(0);  // first tile in flight before the query loads
+  __builtin_amdgcn_sched_barrier(0);
+  // Operand reads of Sᵀ = K·Qᵀ: lane n takes tile row perm_row(n), chunk 2kk + g.
+  const int krow = perm_row(n);
+  const int kr_base = krow * D, kr_swz = k_swz<D>(krow);
 
   // Qᵀ as the B operand: column n is query head hq0 + n (zero past the block's heads).
   bf16x8 qreg[KSTEPS];
@@ -304,14 +339,22 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_gqa_split_kernel(
   float m_run = kNegInf, l_run = 0.f;
   const int nt = (ntok + kGqaTile - 1) / kGqaTile;
 
-  auto step = [&](int t, const bf16x8* kc, bf16x8* kn) {
-    // Tile t-1's V reads (same ring slot as tile t+1) complete before that slot is refilled.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (t + 1 < nt) issue(t + 1, kn);
-    // Sᵀ (32 tokens x 32 heads); tokens past ntok masked.
-    f32x16 st = mfma32(kc[0], qreg[0], f32x16{});
+  for (int t = 0; t < nt; ++t) {
+    // Tile t lands; it moves to LDS and the staging registers take tile t+1
+    // (past the last tile those loads fall outside the buffer: nothing is fetched).
 #pragma unroll
-    for (int kk = 1; kk < KSTEPS; ++kk) st = mfma32(kc[kk], qreg[kk], st);
+    for (int i = 0; i < NLD; ++i) {
+      *reinterpret_cast<u32x4*>(kt + kw_off[i]) = kst[i];
+      *reinterpret_cast<u32x4*>(vt + vw_off[i]) = vst[i];
+    }
+    load(t + 1);
+    // Sᵀ (32 tokens x 32 heads); tokens past ntok masked.
+    f32x16 st = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(kt + kr_base + (((2 * kk + g) ^ kr_swz) << 3));
+      st = mfma32(__builtin_bit_cast(bf16x8, a), qreg[kk], st);
+    }
     float mx = kNegInf;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -343,35 +386,15 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_gqa_split_kernel(
       }
       pb[h] = __builtin_bit_cast(bf16x8, w);
     }
-    // V(t) resident: only tile t+1's loads may still be in flight.
-    if (t + 1 < nt)
-      wait_vm<KSTEPS + NDMA>();
-    else
-      wait_vm<0>();
-    bf16* vs = ring + (t & 1) * VT;
-    if (kGqaTile * (t + 1) > ntok) {  // last tile: rows past ntok must read as zero
-      const int first = ntok - kGqaTile * t;
-      for (int idx = lane; idx < (kGqaTile - first) * CPR; idx += 64) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(vs + (first + idx / CPR) * D + (idx % CPR) * 8) = z;
-      }
-    }
-    // Oᵀ += Vᵀ Pᵀ
+    // Oᵀ += Vᵀ Pᵀ (V rows past ntok were loaded as zeros)
 #pragma unroll
     for (int bb = 0; bb < DBLK; ++bb)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x4 lo = lds_read_tr4(vs + voff[bb] + 16 * kk * D);
-        const bf16x4 hi = lds_read_tr4(vs + voff[bb] + 16 * kk * D + 4 * D);
+        const bf16x4 lo = lds_read_tr4(vt + voff[bb] + 16 * kk * D);
+        const bf16x4 hi = lds_read_tr4(vt + voff[bb] + 16 * kk * D + 4 * D);
         oacc[bb] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb[kk], oacc[bb]);
       }
-  };
-
-  bf16x8 ka[KSTEPS], kb2[KSTEPS];
-  issue(0, ka);
-  for (int t = 0; t < nt; t += 2) {  // unrolled by two so the K register buffers alternate
-    step(t, ka, kb2);
-    if (t + 1 < nt) step(t + 1, kb2, ka);
   }
 
   // Partial of this split for the block's heads: unnormalised Oᵀ column, max, normaliser.
@@ -471,18 +494,25 @@ hipError_t launch(const DecodeArgs& a) {
   return hipGetLastError();
 }
 
+template <int D, int TPW>
+hipError_t launch_gqa_split(const DecodeArgs& a, long long nhb) {
+  const long long units = (long long)a.S * a.max_blocks * (kPage / TPW) * a.Hkv * nhb;
+  const dim3 grid1((unsigned)((units + kDecThreads / 64 - 1) / (kDecThreads / 64))), block1(kDecThreads);
+  hipLaunchKernelGGL((decode_gqa_split_kernel<D, TPW>), grid1, block1, 0, a.stream, static_cast<const bf16*>(a.q),
+                     static_cast<const bf16*>(a.kv_pool), a.block_table, a.seq_lens, a.part, a.S, a.H, a.Hkv,
+                     a.num_pages, a.max_blocks, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_gqa(const DecodeArgs& a) {
   const long long nhb = (a.H / a.Hkv + kGqaCols - 1) / kGqaCols;
-  const long long units = (long long)a.S * a.max_blocks * (kPage / kGqaTokens) * a.Hkv * nhb;
-  const dim3 grid1((unsigned)((units + kDecThreads / 64 - 1) / (kDecThreads / 64))), block1(kDecThreads);
-  hipLaunchKernelGGL((decode_gqa_split_kernel<D>), grid1, block1, 0, a.stream, static_cast<const bf16*>(a.q),
-                     static_cast<const bf16*>(a.kv_pool), a.block_table, a.seq_lens, a.part, a.S, a.H, a.Hkv,
-                     a.num_pages, a.max_blocks, a.scale * kLog2e);
-  hipError_t e = hipGetLastError();
+  // Page-sized splits when the table holds enough (page, key/value head) units.
+  const int split = (long long)a.S * a.max_blocks * a.Hkv * nhb >= kGqaPageUnits ? kPage : kPage / 2;
+  hipError_t e = split == kPage ? launch_gqa_split<D, kPage>(a, nhb) : launch_gqa_split<D, kPage / 2>(a, nhb);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.S * a.H), dim3(64), 0, a.stream, a.part, a.seq_lens,
-                     static_cast<bf16*>(a.o), a.lse, a.H, a.max_blocks, kGqaTokens);
+                     static_cast<bf16*>(a.o), a.lse, a.H, a.max_blocks, split);
   return hipGetLastError();
 }
 

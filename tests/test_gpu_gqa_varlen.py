@@ -182,6 +182,18 @@ def test_decode_gqa_shapes(H, Hkv, d):
     _decode_compare(f"decode H={H} Hkv={Hkv} d={d}", p)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_gqa_page_splits(d):
+    """A block table wide enough (8 sequences x 32 pages x 4 key/value heads)
+    that each wavefront takes a whole page: lengths on, just before and just
+    after page boundaries, a one-token sequence and a nearly full table."""
+    lens = [1, 255, 256, 257, 511, 513, 4000, 8191]
+    p = workloads.paged_inputs(num_seqs=len(lens), H=16, Hkv=4, d=d, max_blocks=32, seed=40 + d,
+                               seq_lens=lens, poison=True, spare_pages=5)
+    print(f"[decode gqa pages] H=16 Hkv=4 d={d}", flush=True)
+    _decode_compare(f"decode pages H=16 Hkv=4 d={d}", p)
+
+
 def test_decode_gqa_is_deterministic():
     p = workloads.paged_inputs(num_seqs=4, H=32, Hkv=8, d=128, len_lo=300, len_hi=3000, max_blocks=12, seed=4)
     args = cuda(p.q, p.kv_pool, p.block_table, p.seq_lens)
