@@ -421,14 +421,16 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_gqa_split_kernel(
 
 // One wavefront per (sequence, head): merge the per-split partial states.
 // Lane j holds split j's (m, l); the output features are split over lanes
-// and the splits' rows are loaded in independent batches of eight.
+// and the splits' rows are loaded in independent batches of 32, the first
+// batch issued together with the (m, l) loads so that a merge of up to 32
+// splits waits on memory once.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ part,
                                                           const int32_t* __restrict__ seq_lens,
                                                           bf16* __restrict__ O, float* __restrict__ LSE, int H,
                                                           int max_blocks, int split) {
   constexpr int PER = D / 64;
-  constexpr int BATCH = 8;
+  constexpr int BATCH = 32;
   const int sh = blockIdx.x;
   const int s = sh / H;
   const int lane = threadIdx.x;
@@ -443,27 +445,36 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
     if (LSE != nullptr && lane == 0) LSE[sh] = kNegInf;
     return;
   }
-  float m = kNegInf, o[PER], lsum = 0.f;
+  float v[BATCH][PER];
+  auto load_rows = [&](int j0) {  // this lane's features of splits j0 .. j0+BATCH-1 (clamped)
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const float* pj = p + (size_t)min(j0 + i, ns - 1) * (D + 2) + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) v[i][e] = pj[e];
+    }
+  };
+  // (m, l) of split `lane` (the first 64 splits), then the first rows.
+  const float m0 = lane < ns ? p[(size_t)lane * (D + 2) + D] : kNegInf;
+  const float l0 = lane < ns ? p[(size_t)lane * (D + 2) + D + 1] : 0.f;
+  load_rows(0);
+  float m = m0, o[PER], lsum = 0.f;
 #pragma unroll
   for (int e = 0; e < PER; ++e) o[e] = 0.f;
-  for (int j0 = 0; j0 < ns; j0 += 64) {
+  for (int j0 = 64; j0 < ns; j0 += 64) {  // more than 64 splits
     const int j = j0 + lane;
     m = fmaxf(m, j < ns ? p[(size_t)j * (D + 2) + D] : kNegInf);
   }
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   for (int j0 = 0; j0 < ns; j0 += 64) {
     const int j = j0 + lane;
-    const float w = j < ns ? exp2_fast(p[(size_t)j * (D + 2) + D] - m) : 0.f;
-    lsum += j < ns ? w * p[(size_t)j * (D + 2) + D + 1] : 0.f;
+    const float mj = j0 == 0 ? m0 : (j < ns ? p[(size_t)j * (D + 2) + D] : kNegInf);
+    const float lj = j0 == 0 ? l0 : (j < ns ? p[(size_t)j * (D + 2) + D + 1] : 0.f);
+    const float w = j < ns ? exp2_fast(mj - m) : 0.f;
+    lsum += w * lj;
     const int cnt = min(64, ns - j0);
     for (int i0 = 0; i0 < cnt; i0 += BATCH) {
-      float v[BATCH][PER];
-#pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
-        const float* pj = p + (size_t)(j0 + min(i0 + i, cnt - 1)) * (D + 2) + lane * PER;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) v[i][e] = pj[e];
-      }
+      if (j0 + i0 > 0) load_rows(j0 + i0);
 #pragma unroll
       for (int i = 0; i < BATCH; ++i) {
         const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), (i0 + i) & 63));
