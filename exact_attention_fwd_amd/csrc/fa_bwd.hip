@@ -410,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
   TileReads<D> rd;
   rd.init(lane);
   auto qview = [&](int i) { return step_head(kv, shape, i / tph, D); };  // as in the kernel above
-  auto first_row = [&](int i) { return qstart + (i % tph) * kTileRows; };
+  auto first_row = [&](int i) { return qstart + (int)((unsigned)i % (unsigned)tph) * kTileRows; };
   // Tile i into a ring slot: Q and dO blocks, and 32 statistics per wave
   // (wave w: rows 32(w & 1).. of LSE for w < 2, of D for w >= 2).
   auto issue = [&](int i, bf16* qslot, bf16* dslot, float* sslot) {
@@ -490,10 +490,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
     // a burst here, where the four wavefronts' bursts queue behind each other in
     // the CU's memory pipeline.  Past the last tile they aim beyond the
     // buffers and fetch nothing, so every step issues the same number of loads.
-    const int i3 = min(t + 3, ntiles - 1);
     const uint32_t bias = t + 3 < ntiles ? 0u : 0xF0000000u;
-    const HeadView hq3 = qview(i3);
-    const int r03 = first_row(i3);
+    const unsigned i3 = (unsigned)min(t + 3, ntiles - 1), j3 = i3 / (unsigned)tph;
+    const HeadView hq3 = step_head(kv, shape, (int)j3, D);
+    const int r03 = qstart + (int)(i3 - j3 * (unsigned)tph) * kTileRows;
     const auto rq3 = make_rsrc(Q + hq3.q_off, (uint32_t)N * hq3.qs * 2);
     const auto rd3 = make_rsrc(dO + hq3.q_off, (uint32_t)N * hq3.qs * 2);
     const auto rs3 = make_rsrc((wave < 2 ? LSE2 : delta) + hq3.st_off, (uint32_t)N * 4);
