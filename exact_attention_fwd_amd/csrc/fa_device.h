@@ -257,6 +257,31 @@ __device__ __forceinline__ void map_unit(int bid, int B, int H, int group, int& 
   h = u / B;
 }
 
+// The same mapping for a grouped-head attention whose every rank of a unit
+// reads the same key/value rows (a paged prefill: each query tile of a chunk
+// streams the cached prefix first).  When an XCD's range of the head-major
+// numbering is whole key/value heads of every batch entry, its blocks go one
+// (batch entry, key/value head) at a time: the `group` query heads x all
+// ranks, heaviest rank first.  The XCD's ~32 concurrent blocks then read one
+// prefix 32 ways instead of 8 prefixes 4 ways (rank by rank), which took the
+// L2 hit rate of a chunked prefill from 31%; every XCD still holds a slice of
+// every batch entry.  Other shapes fall back to map_unit.
+__device__ __forceinline__ void map_unit_kv(int bid, int B, int H, int group, int& rank, int& b, int& h) {
+  const int BH = B * H;
+  const int upx = BH >> 3;
+  if ((BH & 7) != 0 || upx % (B * group) != 0) {
+    map_unit(bid, B, H, group, rank, b, h, true);
+    return;
+  }
+  const int R = gridDim.x / BH;
+  const int slot = bid >> 3;
+  const int per = group * R;                  // blocks of one (batch entry, key/value head)
+  const int k = slot / per, idx = slot % per;
+  rank = idx / group;
+  b = k % B;
+  h = (bid & 7) * (upx / B) + (k / B) * group + idx % group;
+}
+
 // Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {

@@ -472,14 +472,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 }
 
 // The same forward with 64 queries per wavefront, for d = 128 with K/V laid
-// out like the queries (dense, grouped heads, packed batches): four
-// wavefronts per workgroup, one per SIMD.  Each K and Vᵀ operand read from
+// out like the queries (dense, grouped heads, packed batches) or read
+// through a page table (paged prefill): four wavefronts per workgroup, one
+// per SIMD.  Each K and Vᵀ operand read from
 // LDS feeds two products (query blocks j = 0, 1), halving LDS traffic per
 // FLOP; the output accumulators live in accumulation registers.
-template <bool CAUSAL>
+template <bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                                          const bf16* __restrict__ V, bf16* __restrict__ O,
-                                                         float* __restrict__ LSE, AttnShape shape,
+                                                         float* __restrict__ LSE, AttnShape shape, PagedKV pkv,
                                                          float scale_log2) {
   constexpr int D = 128;
   constexpr int KSTEPS = D / 16;
@@ -494,24 +495,53 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
   __shared__ __attribute__((aligned(1024))) bf16 kbuf1[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 vbuf0[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 vbuf1[TILE];
+  __shared__ int ptab[PAGED ? kMaxPrefillPages : 1];  // this sequence's pool pages
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
   int rank, bi, hi;
-  map_unit(blockIdx.x, shape.B, shape.H, shape.H / shape.Hkv, rank, bi, hi, true);
+  if constexpr (PAGED)
+    map_unit_kv(blockIdx.x, shape.B, shape.H, shape.H / shape.Hkv, rank, bi, hi);
+  else
+    map_unit(blockIdx.x, shape.B, shape.H, shape.H / shape.Hkv, rank, bi, hi, true);
   const HeadView hv = head_view(shape, bi, hi, D);
   const int N = hv.L;
   const int nqb = (N + kBR - 1) / kBR;
   if (rank >= nqb) return;
   const int qb = CAUSAL ? nqb - 1 - rank : rank;
   const int q0 = qb * kBR;
-  const int Nk = N;
-  const int kvs = hv.kvs;
+  // Keys of this sequence and the causal offset: query q sees keys 0 .. q + off.
+  int Nk = N, off = 0;
+  const int kvs = PAGED ? shape.Hkv * D : hv.kvs;  // elements between consecutive key rows
+  const int hkv = hi / (shape.H / shape.Hkv);
+  if constexpr (PAGED) {
+    Nk = min(max(pkv.seq_lens[bi], 0), pkv.max_blocks * kPage);
+    off = Nk - N;
+    const int np = (Nk + kPage - 1) / kPage;
+    for (int i = tid; i < np; i += THREADS)
+      ptab[i] = min(max(pkv.block_table[(size_t)bi * pkv.max_blocks + i], 0), pkv.num_pages - 1);
+    __syncthreads();
+  }
   const auto rq = make_rsrc(Q + hv.q_off, (uint32_t)N * hv.qs * 2);
   const auto rk = make_rsrc(K + hv.kv_off, (uint32_t)N * hv.kvs * 2);
   const auto rv = make_rsrc(V + hv.kv_off, (uint32_t)N * hv.kvs * 2);
+  // Paged: key tile t (64 rows) is rows (t % 4)·64.. of pool page ptab[t / 4]
+  // (K half 0, V half 1); the descriptor ends at the sequence's last key, so
+  // later slots are never fetched.  Unpaged: the whole head, offset by the tile.
+  auto tile_rsrc = [&](int t, int half) {
+    if constexpr (PAGED) {
+      const int page = __builtin_amdgcn_readfirstlane(ptab[t >> 2]);
+      const bf16* base = K + ((size_t)page * 2 * kPage + (size_t)half * kPage + (t & 3) * kTileRows) * kvs +
+                         (size_t)hkv * D;
+      return make_rsrc(base, (uint32_t)max(min(kTileRows, Nk - t * kTileRows), 0) * kvs * 2);
+    } else {
+      return half ? rv : rk;
+    }
+  };
+  // Byte offset of tile t inside tile_rsrc(t, ·).
+  auto tile_base = [&](int t) { return PAGED ? 0u : (uint32_t)t * (uint32_t)(64 * kvs * 2); };
   const int qw = q0 + wave * 64;  // this wave's first query; query block j holds qw + 32j ..
 
   // Qᵀ as the B operand of both query blocks (zeros past N).
@@ -539,22 +569,24 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
   const uint32_t drow = (uint32_t)(16 * wave + dma_row) * (uint32_t)(kvs * 2);
   const uint32_t kch = (uint32_t)(dma_pc ^ dma_row) << 4;
   const uint32_t vlane = drow + ((uint32_t)(dma_pc ^ v_swz<D>(dma_row)) << 4);
-  auto issue_k1 = [&](bf16* slot, uint32_t tbase, int i) {
+  auto issue_k1 = [&](bf16* slot, __amdgpu_buffer_rsrc_t r, uint32_t tbase, int i) {
     const uint32_t ch = kch ^ ((uint32_t)(8 * (i & 1) + 4 * (i >> 1)) << 4);
-    lds_dma16(rk, slot + (wave * DMA_PER_WAVE + i) * 512, drow + ch + (tbase + (uint32_t)(4 * i * kvs * 2)));
+    lds_dma16(r, slot + (wave * DMA_PER_WAVE + i) * 512, drow + ch + (tbase + (uint32_t)(4 * i * kvs * 2)));
   };
-  auto issue_v1 = [&](bf16* slot, uint32_t tbase, int i) {
-    lds_dma16(rv, slot + (wave * DMA_PER_WAVE + i) * 512, vlane + (tbase + (uint32_t)(4 * i * kvs * 2)));
+  auto issue_v1 = [&](bf16* slot, __amdgpu_buffer_rsrc_t r, uint32_t tbase, int i) {
+    lds_dma16(r, slot + (wave * DMA_PER_WAVE + i) * 512, vlane + (tbase + (uint32_t)(4 * i * kvs * 2)));
   };
   auto issue_k = [&](bf16* slot, int t) {
+    const auto r = tile_rsrc(t, 0);
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i)
-      lds_dma16(rk, slot + (wave * DMA_PER_WAVE + i) * 512, dma_off(i, false) + (uint32_t)t * (64 * kvs * 2));
+      lds_dma16(r, slot + (wave * DMA_PER_WAVE + i) * 512, dma_off(i, false) + tile_base(t));
   };
   auto issue_v = [&](bf16* slot, int t) {
+    const auto r = tile_rsrc(t, 1);
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i)
-      lds_dma16(rv, slot + (wave * DMA_PER_WAVE + i) * 512, dma_off(i, true) + (uint32_t)t * (64 * kvs * 2));
+      lds_dma16(r, slot + (wave * DMA_PER_WAVE + i) * 512, dma_off(i, true) + tile_base(t));
   };
 
   // LDS operand offsets (elements).  K: rows perm_row(n), 16-byte chunk
@@ -575,7 +607,7 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
 
   // s[2 kb + j]: Sᵀ block of keys 32kb.., queries 32j.. (register r: key crow(kb, r, g), query n).
   auto mask = [&](int k0, f32x16* s) {
-    if ((CAUSAL && k0 + kBC - 1 > qw) || (k0 + kBC > Nk)) {
+    if ((CAUSAL && k0 + kBC - 1 > qw + off) || (k0 + kBC > Nk)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -583,7 +615,7 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + crow(kb, r, g);
-            const bool dead = (key >= Nk) || (CAUSAL && key > qw + 32 * j + n);
+            const bool dead = (key >= Nk) || (CAUSAL && key > qw + 32 * j + n + off);
             s[2 * kb + j][r] = dead ? kNegInf : s[2 * kb + j][r];
           }
     }
@@ -599,10 +631,10 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
   float m_run[2] = {kNegInf, kNegInf};
   float l_run[2] = {0.f, 0.f};
 
-  const int kv_end = CAUSAL ? min(Nk, q0 + kBR) : Nk;
+  const int kv_end = CAUSAL ? max(min(Nk, q0 + kBR + off), 0) : Nk;
   const int ntiles = (kv_end + kBC - 1) / kBC;
-  const int wlast = min(qw + 63, N - 1);
-  const int wnt = (qw >= N) ? 0 : (CAUSAL ? min(ntiles, wlast / kBC + 1) : ntiles);
+  const int wlast = min(qw + 63, N - 1) + off;  // the wave's last visible key (causal)
+  const int wnt = (qw >= N) ? 0 : (CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / kBC + 1)) : ntiles);
 
   if (ntiles > 0) issue_k(kbuf0, 0);
   if (ntiles > 1) issue_k(kbuf1, 1);
@@ -654,8 +686,10 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
   constexpr int DMA0 = 1;
   auto tile_slots = [&](bool maskn, int t, f32x16* sc, f32x16* sn, const bf16* kn, const bf16* vs,
                         bf16* kdma, bf16* vdma) {
-    const uint32_t kt_base = t + 2 < ntiles ? (uint32_t)(t + 2) * (uint32_t)(64 * kvs * 2) : 0xF0000000u;
-    const uint32_t vt_base = t + 1 < ntiles ? (uint32_t)(t + 1) * (uint32_t)(64 * kvs * 2) : 0xF0000000u;
+    const uint32_t kt_base = t + 2 < ntiles ? tile_base(t + 2) : 0xF0000000u;
+    const uint32_t vt_base = t + 1 < ntiles ? tile_base(t + 1) : 0xF0000000u;
+    const auto rk2 = tile_rsrc(min(t + 2, ntiles - 1), 0);
+    const auto rv1 = tile_rsrc(min(t + 1, ntiles - 1), 1);
     auto kread = [&](int i) {
       return *reinterpret_cast<const bf16x8*>(kn + (i / KSTEPS) * 32 * D + koff(i % KSTEPS));
     };
@@ -726,9 +760,9 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
       if constexpr (hs >= DMA0 && (hs - DMA0) % 2 == 0 && (hs - DMA0) / 2 < 2 * DMA_PER_WAVE) {
         constexpr int i = (hs - DMA0) / 2;
         if constexpr (i < DMA_PER_WAVE)
-          issue_k1(kdma, kt_base, i);
+          issue_k1(kdma, rk2, kt_base, i);
         else
-          issue_v1(vdma, vt_base, i - DMA_PER_WAVE);
+          issue_v1(vdma, rv1, vt_base, i - DMA_PER_WAVE);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -786,7 +820,7 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
       return;
     }
     const int k0n = k0 + kBC;
-    tile_slots((CAUSAL && k0n + kBC - 1 > qw) || (k0n + kBC > Nk), t, sc, sn, kn, vc, kc, vn);
+    tile_slots((CAUSAL && k0n + kBC - 1 > qw + off) || (k0n + kBC > Nk), t, sc, sn, kn, vc, kc, vn);
   };
 
   for (int t = 0; t < ntiles; t += 2) {
@@ -894,18 +928,19 @@ hipError_t launch_bf16(const ForwardArgs& a) {
   return hipGetLastError();
 }
 
+template <bool PAGED>
 hipError_t launch_w64(const ForwardArgs& a) {
   const int nqb = (a.s.N + kBR - 1) / kBR;
   const dim3 grid((unsigned)(nqb * a.s.B * a.s.H)), block(256);
   const float sl2 = a.scale * kLog2e;
   auto* q = static_cast<const bf16*>(a.q);
-  auto* k = static_cast<const bf16*>(a.k);
-  auto* v = static_cast<const bf16*>(a.v);
+  auto* k = static_cast<const bf16*>(PAGED ? a.kv.pool : a.k);
+  auto* v = static_cast<const bf16*>(PAGED ? a.kv.pool : a.v);
   auto* o = static_cast<bf16*>(a.o);
   if (a.causal)
-    hipLaunchKernelGGL((fwd_w64_kernel<true>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.s, sl2);
+    hipLaunchKernelGGL((fwd_w64_kernel<true, PAGED>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.s, a.kv, sl2);
   else
-    hipLaunchKernelGGL((fwd_w64_kernel<false>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.s, sl2);
+    hipLaunchKernelGGL((fwd_w64_kernel<false, PAGED>), grid, block, 0, a.stream, q, k, v, o, a.lse, a.s, a.kv, sl2);
   return hipGetLastError();
 }
 
@@ -913,7 +948,7 @@ template <int D>
 hipError_t launch_bf16_any(const ForwardArgs& a) {
   const bool paged = a.kv.pool != nullptr, rope = a.rope.cos != nullptr;
 #if FWD_W64
-  if (D == 128 && !paged && !rope) return launch_w64(a);
+  if (D == 128 && !rope) return paged ? launch_w64<true>(a) : launch_w64<false>(a);
 #endif
   if (paged) return rope ? launch_bf16<D, true, true>(a) : launch_bf16<D, true, false>(a);
   return rope ? launch_bf16<D, false, true>(a) : launch_bf16<D, false, false>(a);
