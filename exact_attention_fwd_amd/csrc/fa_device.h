@@ -257,15 +257,17 @@ __device__ __forceinline__ void map_unit(int bid, int B, int H, int group, int& 
   h = u / B;
 }
 
-// The same mapping for a grouped-head attention whose every rank of a unit
-// reads the same key/value rows (a paged prefill: each query tile of a chunk
-// streams the cached prefix first).  When an XCD's range of the head-major
-// numbering is whole key/value heads of every batch entry, its blocks go one
-// (batch entry, key/value head) at a time: the `group` query heads x all
-// ranks, heaviest rank first.  The XCD's ~32 concurrent blocks then read one
-// prefix 32 ways instead of 8 prefixes 4 ways (rank by rank), which took the
-// L2 hit rate of a chunked prefill from 31%; every XCD still holds a slice of
-// every batch entry.  Other shapes fall back to map_unit.
+// The same mapping for batches of several sequences whose ranks of a unit all
+// read the start of the same key/value rows (a paged prefill: every query tile
+// of a chunk streams the cached prefix first; a packed causal batch: every
+// query tile streams the sequence from its first key).  When an XCD's range of
+// the head-major numbering is whole key/value heads of every batch entry, its
+// blocks go one (batch entry, key/value head) at a time: the `group` query
+// heads x all ranks, heaviest rank first.  The XCD's ~32 concurrent blocks then
+// read one prefix up to 32 ways; rank by rank, a chunked prefill of 8
+// sequences read 8 prefixes 4 ways and hit L2 on 31% of its tile reads (93%
+// this way).  Every XCD still holds a slice of every batch entry.  Other
+// shapes fall back to map_unit.
 __device__ __forceinline__ void map_unit_kv(int bid, int B, int H, int group, int& rank, int& b, int& h) {
   const int BH = B * H;
   const int upx = BH >> 3;

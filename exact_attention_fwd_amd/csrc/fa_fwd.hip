@@ -502,7 +502,7 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
   int rank, bi, hi;
-  if constexpr (PAGED)
+  if (PAGED || shape.cu != nullptr)
     map_unit_kv(blockIdx.x, shape.B, shape.H, shape.H / shape.Hkv, rank, bi, hi);
   else
     map_unit(blockIdx.x, shape.B, shape.H, shape.H / shape.Hkv, rank, bi, hi, true);
