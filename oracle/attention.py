@@ -79,8 +79,11 @@ def _softmax_rows(s: np.ndarray):
     """Two-pass row softmax: m = row max, E = exp(S - m), l = row sum, P = E / l.
 
     A row with no visible key (all -inf) gives P = 0, l = 0 and m = -inf, so
-    its output is 0 and its logsumexp is -inf rather than NaN.
+    its output is 0 and its logsumexp is -inf rather than NaN; so does a row
+    of a sequence with no key at all (zero columns).
     """
+    if s.shape[1] == 0:
+        return np.zeros_like(s), np.full(s.shape[0], NEG_INF)
     m = s.max(axis=1)
     m_safe = np.where(np.isfinite(m), m, 0.0)
     e = np.exp(s - m_safe[:, None])

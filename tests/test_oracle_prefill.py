@@ -75,3 +75,19 @@ def test_query_that_sees_no_key_is_empty():
     # query 1 sees only key 0, so its output is that key's value row
     pool = p.kv_pool.double().numpy()
     np.testing.assert_allclose(o[1], np.repeat(pool[int(p.block_table[0, 0]), 1, 0], 2, axis=0), atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_sequence_without_keys_is_empty(causal):
+    """A sequence with no cached key: every one of its queries has an empty
+    softmax (O = 0, LSE = -inf), and the neighbouring sequence still equals
+    its own prefill computed alone."""
+    p = prefill_inputs([4, 3], [0, 6], H=2, Hkv=1, d=8, seed=8, page_size=4)
+    o, lse = prefill_paged(p.q, p.kv_pool, p.block_table, p.seq_lens_k, p.cu_seqlens_q, causal=causal,
+                           scale=0.5, page_size=4)
+    assert (o[:4] == 0).all() and np.isneginf(lse[:, :4]).all()
+    t0, t1 = _rows(p, 1)
+    o1, l1 = prefill_paged(p.q[t0:t1], p.kv_pool, p.block_table[1:], p.seq_lens_k[1:],
+                           torch.tensor([0, t1 - t0], dtype=torch.int32), causal=causal, scale=0.5, page_size=4)
+    np.testing.assert_allclose(o[t0:t1], o1, atol=1e-15)
+    np.testing.assert_allclose(lse[:, t0:t1], l1, atol=1e-15)
