@@ -258,11 +258,25 @@ def test_prefill_paged_heads(Hkv):
     _prefill_compare(f"prefill Hkv={Hkv}", p, True)
 
 
-def test_prefill_more_queries_than_keys():
-    """Causal rows before the first cached key are empty: O = 0, LSE = -inf."""
-    p = workloads.prefill_inputs([70, 5], [40, 5], H=4, Hkv=4, d=64, seed=3)
-    o, lse = _prefill_compare("prefill n > L", p, True)
-    assert (o[:30] == 0).all() and torch.isneginf(lse[:, :30]).all()
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_more_queries_than_keys(d):
+    """Causal rows before the first cached key are empty: O = 0, LSE = -inf
+    (at d = 128 a whole 64-query wavefront of the first sequence, and part of
+    the next, see no key)."""
+    p = workloads.prefill_inputs([300, 70, 5], [40, 40, 5], H=4, Hkv=4, d=d, seed=3 + d)
+    o, lse = _prefill_compare(f"prefill n > L d={d}", p, True)
+    assert (o[:260] == 0).all() and torch.isneginf(lse[:, :260]).all()
+    assert (o[300:330] == 0).all() and torch.isneginf(lse[:, 300:330]).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_sequence_without_keys(d):
+    """A sequence with no cached key at all: its queries get O = 0 and
+    LSE = -inf; the other sequence of the batch is unaffected."""
+    p = workloads.prefill_inputs([300, 3], [0, 3], H=4, Hkv=2, d=d, seed=11 + d)
+    for causal in (True, False):
+        o, lse = _prefill_compare(f"prefill L=0 d={d} causal={causal}", p, causal)
+        assert (o[:300] == 0).all() and torch.isneginf(lse[:, :300]).all()
 
 
 def test_prefill_without_prefix_matches_varlen_forward():
