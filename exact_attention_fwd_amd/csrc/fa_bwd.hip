@@ -354,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
   constexpr int TILE = kTileRows * D;
   constexpr int NA = 2 * 2 * KSTEPS;  // S and dP products of a tile (two 32-query blocks)
   constexpr int NT = 2 * NA;          // plus as many dV and dK products
-  constexpr int LOOK = 2;
+  constexpr int LOOK = 3;  // half-slots between an operand read and its product (2: ~1% slower)
   constexpr int VMEM_PER_TILE = 2 * TileDma<D>::DPW + 1;  // Q, dO blocks and one statistics load per wave
   __shared__ __attribute__((aligned(1024))) bf16 qs0[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 qs1[TILE];
