@@ -226,6 +226,26 @@ def bench_backward(steps, warmup):
             "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def bench_backward_gqa(steps, warmup, Hkv=4):
+    """The c3 causal backward ([2,16,8192,128]) with the 16 query heads sharing
+    Hkv key/value heads (dK/dV summed over each group)."""
+    import torch
+    import exact_attention_fwd_amd as fa
+    import workloads
+    w = workloads.CONFIGS["c3"]
+    q, k, v, do = (t.to("cuda:0") for t in workloads.gqa_inputs(w.B, w.H, Hkv, w.N, w.d, "bf16", seed=w.seed,
+                                                                 with_dout=True))
+    o, lse = fa.forward(q, k, v, causal=True, scale=w.scale)
+    ws = torch.empty(fa.backward_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda:0")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fn = lambda: fa.backward(q, k, v, o, do, lse, causal=True, scale=w.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
+    avg, med, total = timed_launches(fn, steps, warmup)
+    fl = bwd_flops(w.B, w.H, w.N, w.d, True)
+    return {"workload": f"bwd_gqa_causal_2x16q{Hkv}kv_8192x128", "kernels": "bwd_delta + bwd_dkdv_pipe + bwd_dq",
+            "flops_per_call": fl, "avg_ms": avg, "median_ms": med, "tflops": fl / (avg * 1e-3) / 1e12,
+            "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def bench_decode(steps, warmup, Hkv=None):
     """Paged decode of the 8-sequence configuration; Hkv < 32 stores that many
     key/value heads in the pool (grouped-query decode)."""
@@ -297,7 +317,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["fwd", "fwd32k", "fwdnc", "fwd4k", "bwd", "decode", "copy", "fwdgqa",
-                                       "fwdvarlen", "bwdvarlen", "decodegqa", "prefill"], default=None,
+                                       "fwdvarlen", "bwdvarlen", "decodegqa", "prefill", "bwdgqa"], default=None,
                     help="run one path only (for profiler runs); prints its record")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -323,7 +343,8 @@ def main():
                "fwdvarlen": lambda: bench_varlen(args.steps, args.warmup),
                "bwdvarlen": lambda: bench_varlen(args.steps, args.warmup, backward=True),
                "decodegqa": lambda: bench_decode(args.steps, args.warmup, Hkv=8),
-               "prefill": lambda: bench_prefill(args.steps, args.warmup)}[args.only]()
+               "prefill": lambda: bench_prefill(args.steps, args.warmup),
+               "bwdgqa": lambda: bench_backward_gqa(args.steps, args.warmup)}[args.only]()
         print(json.dumps(rec), flush=True)
         return
 
@@ -336,6 +357,7 @@ def main():
                     ("bwd c3", lambda: bench_backward(max(5, args.steps // 2), 2)),
                     ("decode c4", lambda: bench_decode(args.steps, args.warmup)),
                     ("fwd gqa 32q/8kv", lambda: bench_forward_gqa(max(5, args.steps // 2), 2)),
+                    ("bwd gqa 16q/4kv", lambda: bench_backward_gqa(max(5, args.steps // 2), 2)),
                     ("fwd varlen", lambda: bench_varlen(max(5, args.steps // 2), 2)),
                     ("bwd varlen", lambda: bench_varlen(max(5, args.steps // 2), 2, backward=True)),
                     ("decode c4 gqa 32q/8kv", lambda: bench_decode(args.steps, args.warmup, Hkv=8)),
