@@ -142,12 +142,6 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
   return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
 }
 
-// Sum of a packed pair of bf16 added to an fp32 accumulator (v_dot2_f32_bf16).
-__device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {
-  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
-}
-
 // Swizzle for a row-major [64][D] tile that is read both as a row-major MFMA
 // operand (rows perm_row(m) of 16 lanes, one 16-byte chunk each) and through
 // transposed reads (4 consecutive rows x 4 consecutive chunks per 32 lanes):
@@ -202,12 +196,6 @@ __device__ __forceinline__ HeadView step_head(HeadView v, const Shape& s, int j,
     v.q_off += (size_t)j * D;
     v.st_off += (size_t)j * s.total;
   }
-  return v;
-}
-// Same addressing for a (batch, key/value head) unit (its K/V rows only).
-template <typename Shape>
-__device__ __forceinline__ HeadView kv_head_view(const Shape& s, int b, int hkv, int D) {
-  HeadView v = head_view(s, b, hkv * (s.H / s.Hkv), D);
   return v;
 }
 
