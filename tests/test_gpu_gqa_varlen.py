@@ -119,6 +119,14 @@ def test_varlen_forward_backward(lens, causal, d):
     _varlen_compare(LENS[lens], 4, 2, d, causal, seed=len(LENS[lens]) + d)
 
 
+def test_varlen_blocks_ordered_per_kv_head():
+    """B=2, H=16, Hkv=8: each XCD's share of the head-major units is whole
+    key/value heads of both sequences, so the workgroups take the
+    one-(sequence, key/value head)-at-a-time order; every row must still be
+    produced once."""
+    _varlen_compare([300, 1000], 16, 8, 128, True, seed=21)
+
+
 def test_varlen_mha_and_mqa():
     _varlen_compare([200, 33, 0, 700], 4, 4, 128, True, seed=11)
     _varlen_compare([200, 33, 0, 700], 8, 1, 64, False, seed=12)
@@ -256,6 +264,13 @@ def test_prefill_paged(case, causal, d):
 def test_prefill_paged_heads(Hkv):
     p = workloads.prefill_inputs([130, 40], [900, 40], H=8, Hkv=Hkv, d=128, seed=Hkv)
     _prefill_compare(f"prefill Hkv={Hkv}", p, True)
+
+
+def test_prefill_blocks_ordered_per_kv_head():
+    """B=2, H=32, Hkv=8 (groups of 4): the paged prefill's workgroups take the
+    one-(sequence, key/value head)-at-a-time order."""
+    p = workloads.prefill_inputs([300, 70], [1000, 70], H=32, Hkv=8, d=128, seed=22, poison=True, spare_pages=3)
+    _prefill_compare("prefill ordered blocks", p, True)
 
 
 @pytest.mark.parametrize("d", [64, 128])
