@@ -170,6 +170,16 @@ def test_backward_small(N, causal, d):
     _bwd_compare(f"bwd N={N} d={d} causal={causal}", q, k, v, do, causal, 1 / math.sqrt(d))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_many_units(d):
+    """B=16, H=32: 512 (batch, head) units, 64 per XCD, so every kernel maps
+    its blocks through the grouped order (groups of units, rank by rank)
+    rather than rank by rank over all units; every head is compared."""
+    q, k, v, do = workloads.attention_inputs(16, 32, 130, d, "bf16", seed=500 + d, with_dout=True)
+    _fwd_compare(f"B=16 H=32 N=130 d={d}", q, k, v, True, 1 / math.sqrt(d))
+    _bwd_compare(f"bwd B=16 H=32 N=130 d={d}", q, k, v, do, True, 1 / math.sqrt(d))
+
+
 def test_c3_backward_full_size():
     w = workloads.CONFIGS["c3"]
     print(f"[c3] generating {w.B}x{w.H}x{w.N}x{w.d}", flush=True)
