@@ -305,43 +305,33 @@ def apply_rope(x, positions, cos, sin, interleaved=False):
     return x
 
 
-def _bf16_rne(x32: np.ndarray) -> np.ndarray:
-    """Round fp32 values to bf16, to nearest with ties to even (finite inputs):
-    add 0x7FFF plus the lowest kept bit to the raw fp32 bits, clear the low
-    16 bits."""
-    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+def _bf16_rne(x) -> np.ndarray:
+    """Round real values to bf16 (8 significant bits) to nearest, ties to even,
+    in one step from the fp64 value (no intermediate fp32 rounding): add half
+    of the dropped 45 low mantissa bits of the fp64 encoding, minus one, plus
+    the lowest kept bit, then clear the dropped bits.  Defined for zero and
+    for magnitudes in bf16's normal range [2^-126, 2^128); anything else
+    raises.  Returns fp64 arrays holding the bf16 values."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if not np.all((a == 0) | ((a >= 2.0 ** -126) & (a < 2.0 ** 128))):
+        raise ValueError("bf16 rounding here covers zero and the normal range only")
+    u = x.view(np.uint64)
+    drop = np.uint64(45)
+    keep = (u >> drop) & np.uint64(1)
+    r = (u + np.uint64((1 << 44) - 1) + keep) & ~np.uint64((1 << 45) - 1)
+    return r.view(np.float64)
 
 
 def apply_rope_bf16(x, positions, cos, sin, interleaved=False):
     """The rotation as it is stored for bf16 matrix products.
 
-    The attention products take bf16 operands, so the rotated rows are rounded
-    to bf16 (round-to-nearest-even) — a quantisation of each rotated feature.
-    Both sides take that rounding from the same fp32 value: each feature is
-    computed from the stored bf16 input and the fp32 table entries with IEEE
-    fp32 operations, each product rounded on its own (no fused multiply-add):
-    fl(fl(x·c) − fl(y·s)) and fl(fl(x·s) + fl(y·c)).  Returns fp64 arrays
-    holding those bf16 values; apply_rope is the exact rotation they round.
+    The attention products take bf16 operands, so each rotated feature enters
+    them as a bf16 value: the exact rotation of apply_rope (fp64 arithmetic on
+    the stored bf16 inputs and the fp32 table entries) rounded once to bf16,
+    to nearest with ties to even.  Returns fp64 arrays holding those values.
     """
-    x32 = _f64(x).astype(np.float32)
-    pos = np.asarray(positions)
-    c = _f64(cos).astype(np.float32)[pos]
-    s = _f64(sin).astype(np.float32)[pos]
-    d = x32.shape[-1]
-    if interleaved:
-        a, b = x32[..., 0::2], x32[..., 1::2]
-    else:
-        a, b = x32[..., : d // 2], x32[..., d // 2:]
-    first = np.float32(a * c) - np.float32(b * s)
-    second = np.float32(a * s) + np.float32(b * c)
-    out = np.empty(x32.shape, dtype=np.float64)
-    if interleaved:
-        out[..., 0::2], out[..., 1::2] = _bf16_rne(first), _bf16_rne(second)
-    else:
-        out[..., : d // 2], out[..., d // 2:] = _bf16_rne(first), _bf16_rne(second)
-    return out
+    return _bf16_rne(apply_rope(x, positions, cos, sin, interleaved))
 
 
 def attention_forward_rope(q, k, v, cos, sin, causal=False, scale=None, interleaved=False, cu_seqlens=None,

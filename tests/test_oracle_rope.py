@@ -92,27 +92,61 @@ def test_bf16_rounding_is_nearest_even_on_ties():
         assert got[0, 0] == w and got[0, 1] == 0.0
 
 
-def test_bf16_rounding_matches_torch(rng):
+def test_bf16_rounding_of_fp32_values_matches_torch(rng):
+    # torch rounds an fp32 value to bf16 in one step, so on fp32 inputs it is an
+    # independent implementation of the same rounding
     import torch
     from oracle.attention import _bf16_rne
     x = (rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))).astype(np.float32)
-    ties = (np.arange(1, 2000, dtype=np.uint32) << 16 | 0x8000).view(np.float32)  # exact halfway values
+    ties = ((np.arange(1, 2000, dtype=np.uint32) << 16 | 0x8000) + 0x3F800000).view(np.float32)  # exact halfway values
     for v in (x, ties):
         want = torch.from_numpy(v).to(torch.bfloat16).double().numpy()
         np.testing.assert_array_equal(_bf16_rne(v), want)
 
 
-def test_bf16_rotation_rounds_each_product_separately():
-    # x = 1 + 2^-7, cos = 1 + 2^-23: the exact product 1 + 2^-7 + 2^-23 + 2^-30 rounds to
-    # 1 + 2^-7 + 2^-23 in fp32; y·sin with y = 1, sin = that same fp32 value cancels it
-    # exactly, so the first feature is 0.  A fused multiply-add would keep 2^-30.
+def _bf16_neighbours(x):
+    """The two bf16 values bracketing each fp64 x (x > 0), found by stepping
+    the 8-bit significand of 2^floor(log2 x) — independent of the bit
+    arithmetic under test."""
+    e = np.floor(np.log2(x))
+    ulp = 2.0 ** (e - 7)
+    lo = np.floor(x / ulp) * ulp
+    return lo, lo + ulp, ulp
+
+
+def test_bf16_rounding_of_fp64_values_is_nearest_even(rng):
+    # values with more than 24 significant bits (not fp32-representable), including
+    # ones just off a tie by less than an fp32 ulp, where rounding through fp32 first
+    # would land on the tie and could round the other way
+    x = np.abs(rng.standard_normal(200000)) * np.exp(rng.uniform(-30, 30, 200000))
+    base = (np.arange(1, 3000, dtype=np.uint64) << np.uint64(45)) | np.uint64(1 << 44)  # exact ties
+    ties = (base | (np.uint64(0x3FF) << np.uint64(52))).view(np.float64)
+    near = np.concatenate([ties + 2.0 ** -40, ties - 2.0 ** -40])
+    for v in (x, ties, near):
+        got = oracle.attention._bf16_rne(v)
+        lo, hi, ulp = _bf16_neighbours(v)
+        assert np.all((got == lo) | (got == hi))
+        dlo, dhi = v - lo, hi - v
+        pick_lo = (dlo < dhi) | ((dlo == dhi) & (np.mod(lo / ulp, 2) == 0))
+        np.testing.assert_array_equal(got, np.where(pick_lo, lo, hi))
+        np.testing.assert_array_equal(oracle.attention._bf16_rne(-v), -got)
+    # one step from fp64, not through fp32: 1 + 2^-8 + 2^-40 is above the tie, so it
+    # rounds up, although its nearest fp32 value is the tie itself (which rounds down)
+    assert oracle.attention._bf16_rne(np.array([1 + 2.0**-8 + 2.0**-40]))[0] == 1 + 2.0**-7
+    with pytest.raises(ValueError):
+        oracle.attention._bf16_rne(np.array([2.0**-130]))
+
+
+def test_bf16_rotation_is_one_rounding_of_the_exact_rotation():
+    # x = 1 + 2^-7, cos = 1 + 2^-23, y = 1, sin = 1 + 2^-7 + 2^-23: the exact first feature
+    # (1 + 2^-7)(1 + 2^-23) - (1 + 2^-7 + 2^-23) is 2^-30, a bf16 value; products rounded to
+    # fp32 one by one would cancel to 0 instead
     c32 = np.float32(1 + 2.0**-23)
     s32 = np.float32(1 + 2.0**-7 + 2.0**-23)
     x = np.array([[1 + 2.0**-7, 1.0]])
     got = oracle.apply_rope_bf16(x, [0], np.array([[c32]]), np.array([[s32]]))
-    assert got[0, 0] == 0.0
-    # second feature: fl(x·sin) = 1 + 2^-6 + 2^-14 + 2^-23 (2^-30 dropped), plus y·cos = 1 + 2^-23
-    # gives 2 + 2^-6 + 2^-14 + 2^-22 exactly in fp32, which rounds to 2 + 2^-6 in bf16
+    assert got[0, 0] == 2.0**-30
+    # second feature: 2 + 2^-6 + 2^-14 + 2^-22 + 2^-30 exactly, which rounds to 2 + 2^-6 in bf16
     assert got[0, 1] == 2 + 2.0**-6
 
 
@@ -128,9 +162,8 @@ def test_bf16_rotation_is_the_exact_rotation_rounded(rng, interleaved):
     # representable in bf16
     assert np.array_equal(torch.from_numpy(got).to(torch.bfloat16).double().numpy(), got)
     # within half a bf16 ulp (at most 2^-8 of the value: 8 significant bits) of the exact
-    # value, plus the fp32 steps; and not within 2^-10 everywhere (it is rounded)
-    bound = 2.0**-8 * np.abs(exact) + 2.0**-22 * (np.abs(x) + np.abs(x[..., ::-1])).max() + 1e-30
-    assert np.all(np.abs(got - exact) <= bound)
+    # value; and not within 2^-10 everywhere (it is rounded)
+    assert np.all(np.abs(got - exact) <= 2.0**-8 * np.abs(exact))
     assert np.any(np.abs(got - exact) > 2.0**-10 * np.abs(exact))
     # position 0 (cos 1, sin 0) leaves the stored bf16 rows unchanged
     np.testing.assert_array_equal(oracle.apply_rope_bf16(x[:, :1], [0], c, s, interleaved), x[:, :1])
@@ -146,3 +179,58 @@ def test_default_rotated_forward_uses_the_bf16_rotation(rng):
                                             v, causal=False)
     np.testing.assert_array_equal(o, o2)
     np.testing.assert_array_equal(lse, lse2)
+
+
+# ------------------------------------------ planted mistakes in the rotation
+def _rope_pins():
+    """The pins above as one predicate (used to show they catch planted mistakes)."""
+    rng = np.random.default_rng(9)
+    try:
+        for inter in (False, True):
+            test_rope_is_complex_multiplication(rng, inter)
+        test_bf16_rounding_of_fp64_values_is_nearest_even(rng)
+        test_bf16_rotation_is_one_rounding_of_the_exact_rotation()
+    except AssertionError:
+        return False
+    return True
+
+
+def _truncate_bf16(x):
+    u = np.ascontiguousarray(x, dtype=np.float64).view(np.uint64) & ~np.uint64((1 << 45) - 1)
+    return u.view(np.float64)
+
+
+def _through_fp32(x):
+    import torch
+    return torch.from_numpy(np.asarray(x, dtype=np.float64).astype(np.float32)).to(torch.bfloat16).double().numpy()
+
+
+_exact_rope = oracle.attention.apply_rope
+
+
+def _sin_sign_flipped(x, positions, cos, sin, interleaved=False):
+    return _exact_rope(x, positions, cos, -np.asarray(sin, dtype=np.float64), interleaved)
+
+
+def _pairs_swapped(x, positions, cos, sin, interleaved=False):
+    return _exact_rope(x, positions, cos, sin, not interleaved)
+
+
+ROPE_MUTATIONS = {
+    "bf16 truncation": ("_bf16_rne", _truncate_bf16),
+    "rounded through fp32 first": ("_bf16_rne", _through_fp32),
+    "sine sign flipped": ("apply_rope", _sin_sign_flipped),
+    "half-split and interleaved pairs swapped": ("apply_rope", _pairs_swapped),
+}
+
+
+def test_unmutated_rope_passes_pins():
+    assert _rope_pins()
+
+
+@pytest.mark.parametrize("name", sorted(ROPE_MUTATIONS))
+def test_rope_pins_catch_mutation(monkeypatch, name):
+    attr, fn = ROPE_MUTATIONS[name]
+    monkeypatch.setattr(oracle.attention, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn, raising=False)
+    assert not _rope_pins(), f"mutation '{name}' slipped past the rotation pins"
