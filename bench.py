@@ -284,16 +284,36 @@ def bench_copy(steps, warmup):
             "gbs": 2 * n / (avg * 1e-3) / 1e9}
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(budget_s=20.0):
-    """The fp64 oracle, as it stands, on whole heads of the 16K causal workload."""
-    import numpy as np
+    """The fp64 oracle, as it stands, on whole heads of the 16K causal workload,
+    with its BLAS using every core this process may run on."""
+    import numpy as np  # noqa: F401
     import oracle
     import workloads
+    cores = len(os.sched_getaffinity(0))
+    limiter = None
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
+    except Exception:  # pragma: no cover
+        pass
     try:
         from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=None)
     except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+        blas_threads = None
     w = workloads.CONFIGS["c2a"]
     q, k, v = workloads.workload_inputs(w)
     qf, kf, vf = (x.reshape(w.B * w.H, w.N, w.d) for x in (q, k, v))
@@ -305,8 +325,11 @@ def cpu_baseline(budget_s=20.0):
         done += 1
         if t_total >= budget_s:
             break
+    if limiter is not None:
+        limiter.restore_original_limits()
     fl = fwd_flops(1, 1, w.N, w.d, True) * done
-    return {"value": fl / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    return {"value": fl / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "blas_threads": blas_threads,
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{done} of {w.B * w.H} heads of {w.name} (full causal forward per head, fp64 numpy), "
                       f"{t_total:.1f} s; value = algorithmic flops of the sample / wall time"}
 

@@ -79,6 +79,18 @@ def _check_dev(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _expect(t, shape, dtype, name):
+    """Check a caller-supplied tensor's shape and dtype before any launch: an
+    undersized or mistyped buffer would otherwise be read or written past its
+    end by the kernels."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
 def _call(rc):
     if rc != 0:
         raise FaError(rc)
@@ -93,17 +105,19 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
         raise ValueError("q must be [B, H, N, d] and k, v [B, Hkv, N, d]")
     B, H, N, d = q.shape
     Hkv = k.shape[1]
-    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d or H % Hkv:
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d or Hkv == 0 or H % Hkv:
         raise ValueError("k, v must be [B, Hkv, N, d] with Hkv dividing H")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share a dtype")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if not return_lse:
+        lse = None
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (B, H, N), torch.float32, "lse")
     o = torch.empty_like(q) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if not return_lse:
-        lse = None
     _check_dev(q, k, v, o, lse)
     with torch.cuda.device(q.device):
         if Hkv == H:
@@ -120,6 +134,9 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, s
                    out=None, lse=None, return_lse: bool = True):
     """Packed variable-length forward: q [total, H, d], k/v [total, Hkv, d],
     cu_seqlens int32 [B+1] on the GPU (sequence b = rows cu[b]..cu[b+1]-1).
+    max_seqlen must be >= every length (cu_seqlens is not read on the host):
+    a longer sequence is not computed past max_seqlen and its written rows
+    are NaN in o and lse.
     Returns (o [total, H, d], lse fp32 [H, total] or None)."""
     torch = _torch()
     if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2]:
@@ -129,13 +146,19 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, s
     total, H, d = q.shape
     Hkv = k.shape[1]
     B = cu_seqlens.numel() - 1
+    if Hkv == 0 or H % Hkv:
+        raise ValueError("k, v must be [total, Hkv, d] with Hkv dividing H")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if not return_lse:
+        lse = None
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (H, total), torch.float32, "lse")
     o = torch.empty_like(q) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
-    if not return_lse:
-        lse = None
     _check_dev(q, k, v, cu_seqlens, o, lse)
     with torch.cuda.device(q.device):
         _call(lib().fa_forward_varlen(_dtype_code(q), B, H, Hkv, int(max_seqlen), total, d, _ptr(cu_seqlens), _ptr(q),
@@ -153,12 +176,21 @@ def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = 
     """Recomputing backward; returns (dq, dk, dv) bf16 with dk, dv shaped like k, v
     (grouped key/value heads sum their query heads' gradients)."""
     torch = _torch()
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, N, d] and k, v [B, Hkv, N, d]")
     B, H, N, d = q.shape
     Hkv = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d or Hkv == 0 or H % Hkv:
+        raise ValueError("k, v must be [B, Hkv, N, d] with Hkv dividing H")
     if o.shape != q.shape or dout.shape != q.shape or v.shape != k.shape:
         raise ValueError("o, dout must be shaped like q and v like k")
+    if any(t.dtype != q.dtype for t in (k, v, o, dout)):
+        raise TypeError("q, k, v, o, dout must share a dtype")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32:
         raise ValueError("lse must be fp32 [B, H, N]")
+    _expect(dq, q.shape, q.dtype, "dq")
+    _expect(dk, k.shape, q.dtype, "dk")
+    _expect(dv, v.shape, q.dtype, "dv")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
@@ -184,13 +216,27 @@ def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = 
 
 def backward_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: int, causal: bool = False,
                     scale: float | None = None, workspace=None, dq=None, dk=None, dv=None):
-    """Backward of forward_varlen (same packed layouts; lse fp32 [H, total])."""
+    """Backward of forward_varlen (same packed layouts; lse fp32 [H, total]);
+    max_seqlen as there (a longer sequence gets NaN gradients)."""
     torch = _torch()
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [total, H, d] and k, v [total, Hkv, d]")
     total, H, d = q.shape
     Hkv = k.shape[1]
+    if k.shape[0] != total or k.shape[2] != d or Hkv == 0 or H % Hkv:
+        raise ValueError("k, v must be [total, Hkv, d] with Hkv dividing H")
+    if o.shape != q.shape or dout.shape != q.shape or v.shape != k.shape:
+        raise ValueError("o, dout must be shaped like q and v like k")
+    if any(t.dtype != q.dtype for t in (k, v, o, dout)):
+        raise TypeError("q, k, v, o, dout must share a dtype")
+    if cu_seqlens.dim() != 1 or cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32 [B+1]")
     B = cu_seqlens.numel() - 1
     if lse.shape != (H, total) or lse.dtype != torch.float32:
         raise ValueError("lse must be fp32 [H, total]")
+    _expect(dq, q.shape, q.dtype, "dq")
+    _expect(dk, k.shape, q.dtype, "dk")
+    _expect(dv, v.shape, q.dtype, "dv")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
@@ -219,8 +265,11 @@ def decode_paged(q, kv_pool, block_table, seq_lens, scale: float | None = None, 
     [S, max_blocks] int32, seq_lens [S] int32 (all on the GPU).
     Returns (o [S, H, d] bf16, lse [S, H] fp32 or None)."""
     torch = _torch()
+    if q.dim() != 3:
+        raise ValueError("q must be [S, H, d]")
     S, H, d = q.shape
-    if kv_pool.dim() != 5 or kv_pool.shape[1] != 2 or kv_pool.shape[4] != d or H % kv_pool.shape[3]:
+    if (kv_pool.dim() != 5 or kv_pool.shape[1] != 2 or kv_pool.shape[4] != d or kv_pool.shape[3] == 0
+            or H % kv_pool.shape[3]):
         raise ValueError("kv_pool must be [pages, 2, page_size, Hkv, d] with Hkv dividing H")
     if block_table.dim() != 2 or block_table.shape[0] != S or block_table.dtype != torch.int32:
         raise ValueError("block_table must be int32 [S, max_blocks]")
@@ -232,11 +281,13 @@ def decode_paged(q, kv_pool, block_table, seq_lens, scale: float | None = None, 
         scale = 1.0 / math.sqrt(d)
     P, _, page, Hkv, _ = kv_pool.shape
     mb = block_table.shape[1]
+    if not return_lse:
+        lse = None
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (S, H), torch.float32, "lse")
     o = torch.empty_like(q) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((S, H), dtype=torch.float32, device=q.device)
-    if not return_lse:
-        lse = None
     need = decode_workspace_bytes(S, H, d, mb)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -281,28 +332,42 @@ def forward_rope(q, k, v, rope_cos, rope_sin, causal: bool = False, scale: float
     torch = _torch()
     packed = cu_seqlens is not None
     if packed:
+        if q.dim() != 3 or k.dim() != 3 or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2]:
+            raise ValueError("packed q must be [total, H, d] and k, v [total, Hkv, d]")
+        if cu_seqlens.dim() != 1 or cu_seqlens.dtype != torch.int32 or max_seqlen is None:
+            raise ValueError("packed form needs cu_seqlens int32 [B+1] and max_seqlen")
         total, H, d = q.shape
         Hkv = k.shape[1]
         B = cu_seqlens.numel() - 1
         N = int(max_seqlen)
         lse_shape = (H, total)
     else:
+        if q.dim() != 4 or k.dim() != 4:
+            raise ValueError("q must be [B, H, N, d] and k, v [B, Hkv, N, d]")
         B, H, N, d = q.shape
         Hkv = k.shape[1]
+        if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+            raise ValueError("k, v must be [B, Hkv, N, d]")
         total = 0
         lse_shape = (B, H, N)
-    if v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("k and v must match and share q's dtype")
+    if Hkv == 0 or H % Hkv:
+        raise ValueError("the key/value heads must divide the query heads")
+    if v.shape != k.shape:
+        raise ValueError("k and v must have the same shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
     cos_t, sin_t, rows = _rope_args(rope_cos, rope_sin, d)
     if cos_t is None:
         raise ValueError("forward_rope needs the rotary tables")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if not return_lse:
+        lse = None
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, lse_shape, torch.float32, "lse")
     o = torch.empty_like(q) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
-    if not return_lse:
-        lse = None
     _check_dev(q, k, v, cos_t, sin_t, o, lse, *( [cu_seqlens] if packed else [] ))
     with torch.cuda.device(q.device):
         _call(lib().fa_forward_rope(_dtype_code(q), B, H, Hkv, N, total, d, _ptr(cu_seqlens), _ptr(q), _ptr(k),
@@ -328,7 +393,7 @@ def prefill_paged(q, kv_pool, block_table, seq_lens_k, cu_seqlens_q, max_seqlen_
     total, H, d = q.shape
     P, _, page, Hkv, _ = kv_pool.shape
     B = cu_seqlens_q.numel() - 1
-    if H % Hkv:
+    if Hkv == 0 or H % Hkv:
         raise ValueError("the pool's key/value heads must divide the query heads")
     if cu_seqlens_q.dtype != torch.int32 or seq_lens_k.dtype != torch.int32 or block_table.dtype != torch.int32:
         raise ValueError("cu_seqlens_q, seq_lens_k and block_table must be int32")
@@ -338,11 +403,13 @@ def prefill_paged(q, kv_pool, block_table, seq_lens_k, cu_seqlens_q, max_seqlen_
         raise TypeError("paged prefill takes bf16 q and kv_pool")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if not return_lse:
+        lse = None
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (H, total), torch.float32, "lse")
     o = torch.empty_like(q) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
-    if not return_lse:
-        lse = None
     cos_t, sin_t, rows = _rope_args(rope_cos, rope_sin, d)
     _check_dev(q, kv_pool, block_table, seq_lens_k, cu_seqlens_q, o, lse, cos_t, sin_t)
     with torch.cuda.device(q.device):

@@ -30,10 +30,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-#ifndef BWD_PIPE
-#define BWD_PIPE 1
-#endif
-
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
@@ -315,15 +311,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   if (kw >= N || key >= N) return;
   bf16* dKrow = dK + kv.kv_off + (size_t)key * kv.kvs;
   bf16* dVrow = dV + kv.kv_off + (size_t)key * kv.kvs;
+  const float ks = kv.cut ? kNaN : scale, vs = kv.cut ? kNaN : 1.f;
 #pragma unroll
   for (int b = 0; b < DBLK; ++b)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       u32x2 wk, wv;
-      wk[0] = pack_bf16x2(dk[b][4 * i] * scale, dk[b][4 * i + 1] * scale);
-      wk[1] = pack_bf16x2(dk[b][4 * i + 2] * scale, dk[b][4 * i + 3] * scale);
-      wv[0] = pack_bf16x2(dv[b][4 * i], dv[b][4 * i + 1]);
-      wv[1] = pack_bf16x2(dv[b][4 * i + 2], dv[b][4 * i + 3]);
+      wk[0] = pack_bf16x2(dk[b][4 * i] * ks, dk[b][4 * i + 1] * ks);
+      wk[1] = pack_bf16x2(dk[b][4 * i + 2] * ks, dk[b][4 * i + 3] * ks);
+      wv[0] = pack_bf16x2(dv[b][4 * i] * vs, dv[b][4 * i + 1] * vs);
+      wv[1] = pack_bf16x2(dv[b][4 * i + 2] * vs, dv[b][4 * i + 3] * vs);
       *reinterpret_cast<u32x2*>(dKrow + 32 * b + 8 * i + 4 * g) = wk;
       *reinterpret_cast<u32x2*>(dVrow + 32 * b + 8 * i + 4 * g) = wv;
     }
@@ -580,6 +577,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
   if (kw >= N || key_e >= N) return;
   bf16* dKrow = dK + kv.kv_off + (size_t)key_e * kv.kvs;
   bf16* dVrow = dV + kv.kv_off + (size_t)key_e * kv.kvs;
+  const float ks = kv.cut ? kNaN : scale, vs = kv.cut ? kNaN : 1.f;
   // one accumulator block at a time out of the AGPRs
   static_for<0, DBLK>([&](auto bc) __attribute__((always_inline)) {
     constexpr int bb = decltype(bc)::value;
@@ -587,10 +585,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_pipe_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       u32x2 wk, wv;
-      wk[0] = pack_bf16x2(dk[bb][4 * i] * scale, dk[bb][4 * i + 1] * scale);
-      wk[1] = pack_bf16x2(dk[bb][4 * i + 2] * scale, dk[bb][4 * i + 3] * scale);
-      wv[0] = pack_bf16x2(dv[bb][4 * i], dv[bb][4 * i + 1]);
-      wv[1] = pack_bf16x2(dv[bb][4 * i + 2], dv[bb][4 * i + 3]);
+      wk[0] = pack_bf16x2(dk[bb][4 * i] * ks, dk[bb][4 * i + 1] * ks);
+      wk[1] = pack_bf16x2(dk[bb][4 * i + 2] * ks, dk[bb][4 * i + 3] * ks);
+      wv[0] = pack_bf16x2(dv[bb][4 * i] * vs, dv[bb][4 * i + 1] * vs);
+      wv[1] = pack_bf16x2(dv[bb][4 * i + 2] * vs, dv[bb][4 * i + 3] * vs);
       *reinterpret_cast<u32x2*>(dKrow + 32 * bb + 8 * i + 4 * g) = wk;
       *reinterpret_cast<u32x2*>(dVrow + 32 * bb + 8 * i + 4 * g) = wv;
     }
@@ -751,13 +749,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
   if (qw >= N || qrow >= N) return;
   bf16* row = dQ + hv.q_off + (size_t)qrow * hv.qs;
+  const float qs = hv.cut ? kNaN : scale;
 #pragma unroll
   for (int b = 0; b < DBLK; ++b)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       u32x2 w;
-      w[0] = pack_bf16x2(dq[b][4 * i] * scale, dq[b][4 * i + 1] * scale);
-      w[1] = pack_bf16x2(dq[b][4 * i + 2] * scale, dq[b][4 * i + 3] * scale);
+      w[0] = pack_bf16x2(dq[b][4 * i] * qs, dq[b][4 * i + 1] * qs);
+      w[1] = pack_bf16x2(dq[b][4 * i + 2] * qs, dq[b][4 * i + 3] * qs);
       *reinterpret_cast<u32x2*>(row + 32 * b + 8 * i + 4 * g) = w;
     }
 }
@@ -781,7 +780,7 @@ hipError_t launch(const BackwardArgs& a) {
   const int tiles = (a.s.N + 127) / 128;
   const dim3 grid_kv((unsigned)(tiles * a.s.B * a.s.Hkv)), grid_q((unsigned)(tiles * a.s.B * a.s.H)), block(kThreads);
   if (a.causal) {
-    if (D == 128 && BWD_PIPE)
+    if constexpr (D == 128)
       hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<true>), grid_kv, block, 0, a.stream, q, k, v, dout, a.lse2, a.delta,
                          static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.s, a.scale, sl2);
     else
@@ -792,7 +791,7 @@ hipError_t launch(const BackwardArgs& a) {
     hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid_q, block, 0, a.stream, q, k, v, dout, a.lse, a.delta,
                        static_cast<bf16*>(a.dq), a.s, a.scale, sl2);
   } else {
-    if (D == 128 && BWD_PIPE)
+    if constexpr (D == 128)
       hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<false>), grid_kv, block, 0, a.stream, q, k, v, dout, a.lse2, a.delta,
                          static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.s, a.scale, sl2);
     else

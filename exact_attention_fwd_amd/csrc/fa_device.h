@@ -35,6 +35,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kNaN = __builtin_nanf("");
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -155,10 +156,13 @@ __device__ __forceinline__ int dual_swz(int r) {
 
 // Addressing of one (batch, query head) unit: element offsets of row 0 in
 // Q/O (and dQ/dO), in K/V (and dK/dV) and in LSE/D, the row strides in
-// elements, and the sequence length.
+// elements, and the sequence length.  `cut` is set when a packed sequence is
+// longer than the launch's maximum length: its rows past that length are not
+// computed, so the rows that are get NaN outputs (the call's error made
+// visible instead of a silently partial result).
 struct HeadView {
   size_t q_off, kv_off, st_off;
-  int L, qs, kvs;
+  int L, qs, kvs, cut;
 };
 template <typename Shape>
 __device__ __forceinline__ HeadView head_view(const Shape& s, int b, int h, int D) {
@@ -166,6 +170,7 @@ __device__ __forceinline__ HeadView head_view(const Shape& s, int b, int h, int 
   const int hkv = h / (s.H / s.Hkv);
   if (s.cu == nullptr) {
     v.L = s.N;
+    v.cut = 0;
     v.qs = D;
     v.kvs = D;
     v.q_off = ((size_t)b * s.H + h) * (size_t)s.N * D;
@@ -177,6 +182,7 @@ __device__ __forceinline__ HeadView head_view(const Shape& s, int b, int h, int 
     const int t0 = min(max(s.cu[b], 0), s.total);
     const int t1 = min(max(s.cu[b + 1], t0), s.total);
     v.L = min(t1 - t0, s.N);
+    v.cut = (t1 - t0) > s.N;
     v.qs = s.H * D;
     v.kvs = s.Hkv * D;
     v.q_off = (size_t)t0 * s.H * D + (size_t)h * D;

@@ -51,40 +51,64 @@ __device__ __forceinline__ void max3_here(float& m, float a, float b) {
 constexpr float kRescaleThreshold = 8.0f;
 
 constexpr int kPage = 256;  // tokens per page of a paged key/value pool
-#ifndef FWD_LOOK
-#define FWD_LOOK 2
-#endif
-#ifndef FWD_W64
-#define FWD_W64 1
-#endif
+// Slots between an LDS operand read and the product that consumes it.
+constexpr int kLook = 2;
+
+// bf16 bits of x rounded to nearest (ties to even) in one step from fp64:
+// add half of the 45 dropped mantissa bits (minus one, plus the lowest kept
+// bit) and clear them; the result is exact in fp32, whose top half it is.
+__device__ __forceinline__ uint32_t bf16_rne_f64(double x) {
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  u = (u + ((1ull << 44) - 1) + ((u >> 45) & 1)) & ~((1ull << 45) - 1);
+  return __float_as_uint((float)__longlong_as_double((long long)u)) >> 16;
+}
+
+// Rotation of one feature pair (a, b) by (c, s), rounded to bf16: the exact
+// rotation (a·c − b·s, a·s + b·c) rounded to nearest.  Computed in fp32, whose
+// error is below e = 2^-21·(|a|+|b|)·(|c|+|s|); when the bf16 roundings of
+// r − e and r + e agree, every value in between (the exact one included)
+// rounds the same way.  Otherwise (rare: r within e of a rounding boundary)
+// the lane recomputes the pair in fp64, where the products of bf16 and fp32
+// values are exact and only the sum is rounded, and rounds that directly.
+__device__ __forceinline__ void rotate_pair(float a, float b, float c, float s, uint32_t& ox, uint32_t& oy) {
+  const float xr = __builtin_fmaf(a, c, -(b * s));
+  const float yr = __builtin_fmaf(a, s, b * c);
+  const float e = (__builtin_fabsf(a) + __builtin_fabsf(b)) * (__builtin_fabsf(c) + __builtin_fabsf(s)) * 0x1p-21f;
+  const uint32_t wx = pack_bf16x2(xr - e, xr + e), wy = pack_bf16x2(yr - e, yr + e);
+  ox = pack_bf16x2(xr, xr) & 0xffffu;
+  oy = pack_bf16x2(yr, yr) & 0xffffu;
+  if (((wx ^ (wx >> 16)) | (wy ^ (wy >> 16))) & 0xffffu) {
+    const double ad = a, bd = b, cd = c, sd = s;
+    ox = bf16_rne_f64(ad * cd - bd * sd);
+    oy = bf16_rne_f64(ad * sd + bd * cd);
+  }
+}
 
 // Rotate the feature pairs (x[j], y[j]) of 8 bf16 values each by the angles
-// whose cosines / sines are c[j], s[j]; bf16 (RNE) results.  Each product is
-// rounded to fp32 on its own (no fused multiply-add), so the value that is
-// rounded to bf16 is fl(fl(x·c) − fl(y·s)), fl(fl(x·s) + fl(y·c)) exactly.
+// whose cosines / sines are c[j], s[j] (rotate_pair per pair).
 __device__ __forceinline__ void rotate8(bf16x8& x, bf16x8& y, const float* c, const float* s) {
-#pragma clang fp contract(off)
-  float xr[8], yr[8];
+  u32x4 wx, wy;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float a = (float)x[j], b = (float)y[j];
-    xr[j] = a * c[j] - b * s[j];
-    yr[j] = a * s[j] + b * c[j];
+  for (int j = 0; j < 8; j += 2) {
+    uint32_t x0, y0, x1, y1;
+    rotate_pair((float)x[j], (float)y[j], c[j], s[j], x0, y0);
+    rotate_pair((float)x[j + 1], (float)y[j + 1], c[j + 1], s[j + 1], x1, y1);
+    wx[j / 2] = x0 | (x1 << 16);
+    wy[j / 2] = y0 | (y1 << 16);
   }
-  x = pack8(xr);
-  y = pack8(yr);
+  x = __builtin_bit_cast(bf16x8, wx);
+  y = __builtin_bit_cast(bf16x8, wy);
 }
 // Same for the interleaved pairing: pairs (x[2j], x[2j+1]), angles c[j], s[j].
 __device__ __forceinline__ void rotate8_interleaved(bf16x8& x, const float* c, const float* s) {
-#pragma clang fp contract(off)
-  float r[8];
+  u32x4 w;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float a = (float)x[2 * j], b = (float)x[2 * j + 1];
-    r[2 * j] = a * c[j] - b * s[j];
-    r[2 * j + 1] = a * s[j] + b * c[j];
+    uint32_t r0, r1;
+    rotate_pair((float)x[2 * j], (float)x[2 * j + 1], c[j], s[j], r0, r1);
+    w[j] = r0 | (r1 << 16);
   }
-  x = pack8(r);
+  x = __builtin_bit_cast(bf16x8, w);
 }
 template <int N>
 __device__ __forceinline__ void load_f32(float* dst, const float* src) {
@@ -347,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // tail tile (maskn) is masked and its max retaken after the slots.  Every
   // LDS operand is read LOOK slots ahead of its product; the fences keep the
   // compiler from undoing the order.
-  constexpr int LOOK = FWD_LOOK;
+  constexpr int LOOK = kLook;
   constexpr int NS = 2 * KSTEPS;     // products of S(t+1)
   constexpr int NP = 4 * DBLK;       // products of Oᵀ += Vᵀ·Pᵀ
   constexpr int NT = NS + NP;
@@ -457,7 +481,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const float l_tot = xhalf_sum(l_run);
   // A query that sees no key (paged causal prefill with fewer keys than queries
   // before it) has an empty softmax: O = 0, LSE = -inf.
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = hv.cut ? kNaN : (l_tot > 0.f ? 1.f / l_tot : 0.f);
   bf16* Orow = O + hv.q_off + (size_t)qrow * hv.qs;
 #pragma unroll
   for (int b = 0; b < DBLK; ++b)
@@ -468,7 +492,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       w[1] = pack_bf16x2(oacc[b][4 * i + 2] * inv, oacc[b][4 * i + 3] * inv);
       *reinterpret_cast<u32x2*>(Orow + 32 * b + 8 * i + 4 * g) = w;
     }
-  if (LSE != nullptr && g == 0) LSE[hv.st_off + qrow] = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : kNegInf;
+  if (LSE != nullptr && g == 0)
+    LSE[hv.st_off + qrow] = hv.cut ? kNaN : (l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : kNegInf);
 }
 
 // The same forward with 64 queries per wavefront, for d = 128 with K/V laid
@@ -672,7 +697,7 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
   // One tile: NS slots of S(t+1) (one K read, two products each), then NP
   // slots of Oᵀ += Vᵀ·Pᵀ (one Vᵀ read, two products each); P(t) pairs and
   // the max of S(t+1) ride along as in the 32-query kernel.
-  constexpr int LOOK = FWD_LOOK;
+  constexpr int LOOK = kLook;
   constexpr int NS = 2 * KSTEPS;
   constexpr int NP = 4 * DBLK;
   constexpr int NT = NS + NP;
@@ -834,7 +859,7 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
     const int qrow = qw + 32 * j + n;
     if (qrow >= N) continue;
     const float l_tot = xhalf_sum(l_run[j]);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = hv.cut ? kNaN : (l_tot > 0.f ? 1.f / l_tot : 0.f);
     bf16* Orow = O + hv.q_off + (size_t)qrow * hv.qs;
 #pragma unroll
     for (int b = 0; b < DBLK; ++b)
@@ -846,7 +871,7 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
         *reinterpret_cast<u32x2*>(Orow + 32 * b + 8 * i + 4 * g) = w;
       }
     if (LSE != nullptr && g == 0)
-      LSE[hv.st_off + qrow] = l_tot > 0.f ? (m_run[j] + log2_fast(l_tot)) * kLn2 : kNegInf;
+      LSE[hv.st_off + qrow] = hv.cut ? kNaN : (l_tot > 0.f ? (m_run[j] + log2_fast(l_tot)) * kLn2 : kNegInf);
   }
 }
 
@@ -904,10 +929,10 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
     }
   }
   if (row >= N) return;
-  const float inv = 1.f / l;
+  const float inv = hv.cut ? kNaN : 1.f / l;
 #pragma unroll
   for (int d = 0; d < D; ++d) O[hv.q_off + (size_t)row * hv.qs + d] = acc[d] * inv;
-  if (LSE != nullptr) LSE[hv.st_off + row] = m + logf(l);
+  if (LSE != nullptr) LSE[hv.st_off + row] = hv.cut ? kNaN : m + logf(l);
 }
 
 template <int D, bool PAGED, bool ROPE>
@@ -947,9 +972,7 @@ hipError_t launch_w64(const ForwardArgs& a) {
 template <int D>
 hipError_t launch_bf16_any(const ForwardArgs& a) {
   const bool paged = a.kv.pool != nullptr, rope = a.rope.cos != nullptr;
-#if FWD_W64
   if (D == 128 && !rope) return paged ? launch_w64<true>(a) : launch_w64<false>(a);
-#endif
   if (paged) return rope ? launch_bf16<D, true, true>(a) : launch_bf16<D, true, false>(a);
   return rope ? launch_bf16<D, false, true>(a) : launch_bf16<D, false, false>(a);
 }

@@ -142,7 +142,12 @@ fa_status fa_forward_gqa(fa_dtype dt, int B, int H, int Hkv, int N, int d,
  *               each length to max_seqlen, so a malformed table never makes
  *               them touch memory outside the buffers, but rows it leaves
  *               uncovered are not written.
- *   max_seqlen  the largest length (host value; sizes the launch).
+ *   max_seqlen  the largest length (host value; sizes the launch).  It must
+ *               be >= every sequence's length: rows of a longer sequence past
+ *               max_seqlen are not computed (nor written), and the rows of
+ *               that sequence that are written get NaN in O and the LSE, so
+ *               the error shows in the outputs (the table lives on the device
+ *               and is not read on the host).
  *   q, o        [total, H, d];  k, v  [total, Hkv, d] (token-major, heads
  *               interleaved per token).
  *   lse         [H, total] fp32 or NULL.
@@ -165,7 +170,9 @@ fa_status fa_backward_gqa(fa_dtype dt, int B, int H, int Hkv, int N, int d,
 /* Workspace of fa_backward_varlen in bytes: one fp32 per (head, packed row). */
 size_t fa_backward_varlen_workspace_bytes(int H, int total, int d);
 
-/* Backward of fa_forward_varlen (packed layouts as there; lse [H, total]). */
+/* Backward of fa_forward_varlen (packed layouts as there; lse [H, total]).
+ * As there, max_seqlen must cover every sequence: a longer sequence gets NaN
+ * gradients in the rows that are written and none past max_seqlen. */
 fa_status fa_backward_varlen(fa_dtype dt, int B, int H, int Hkv, int max_seqlen, int total, int d,
                              const int32_t* cu_seqlens, const void* q, const void* k, const void* v,
                              const void* o, const void* dout, const float* lse,
@@ -246,7 +253,9 @@ fa_status fa_decode_paged_gqa(int num_seqs, int H, int Hkv, int d, int page_size
  * prefix caching of zwxr.cn §5.2.
  *   cu_seqlens_q  [B+1] int32 (device): sequence b's queries are packed rows
  *                 cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q.
- *   max_seqlen_q  largest chunk (host value; sizes the launch).
+ *   max_seqlen_q  largest chunk (host value; sizes the launch); a longer
+ *                 chunk is handled as fa_forward_varlen handles a sequence
+ *                 longer than max_seqlen (NaN in its written rows).
  *   q, o          [total_q, H, d] bf16; lse [H, total_q] fp32 or NULL.
  *   kv_pool       [num_pages, 2, 256, Hkv, d] bf16; query head h reads
  *                 key/value head h / (H / Hkv).

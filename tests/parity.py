@@ -4,15 +4,14 @@ Tolerances (per output tensor, GPU value upcast vs the fp64 oracle, over every
 compared element): bf16 outputs max-abs <= 2e-2 and mean-abs <= 2e-3; the
 fp32 forward max-abs <= 1e-4; the logsumexp max-abs <= 1e-3.
 
-Grouped key/value heads: dK and dV of a key/value head are the sum of the g
-query heads' contributions.  Each contribution is computed exactly as one
-ungrouped head (same bound), the contributions' rounding errors come from
-independent bf16 roundings of different heads' P and dS and add like
-independent noise, and the magnitude of the sum (hence its final bf16
-rounding) grows the same way, so the bound on a grouped gradient is the
-ungrouped one times sqrt(g).  With g = 1 it is the bound above.
+Gradients summed over a group of query heads (dK, dV of a shared key/value
+head): the sum of g heads' contributions can reach magnitudes where a bf16
+value's own spacing exceeds the bound (|x| >= 8: half an ulp is 2^-5 > 2e-2),
+so even the exact gradient rounded to bf16 would fail a plain 2e-2.  There the
+max-abs bound applies to the error beyond that unavoidable output rounding:
+per element |got - ref| <= 2e-2 + half a bf16 ulp of ref (check_rounded); the
+mean-abs bound is unchanged.  Every other output keeps the plain bounds.
 """
-import math
 import sys
 
 import numpy as np
@@ -20,11 +19,6 @@ import numpy as np
 BF16_MAX, BF16_MEAN = 2e-2, 2e-3
 F32_MAX = 1e-4
 LSE_MAX = 1e-3
-
-
-def grouped(tol, g):
-    """Bound on a gradient summed over a group of g query heads."""
-    return tol * math.sqrt(g)
 
 
 def to64(t):
@@ -42,6 +36,41 @@ def errors(got, ref):
         return float("inf"), float("inf")
     e = np.abs(got - ref)
     return float(e.max()), float(e.mean())
+
+
+def bf16_half_ulp(x):
+    """Half the spacing of bf16 values around each |x| (8 significant bits):
+    2^(floor(log2|x|) - 8); 0 where x is 0."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    out = np.zeros_like(a)
+    nz = a > 0
+    out[nz] = np.exp2(np.floor(np.log2(a[nz])) - 8)
+    return out
+
+
+def check_rounded(name, got, ref, max_tol=BF16_MAX, mean_tol=BF16_MEAN):
+    """Bound for bf16 outputs that may exceed the magnitude where their own
+    rounding fits the max-abs bound: every element within max_tol plus half a
+    bf16 ulp of the reference value, and the mean-abs bound as usual.  Prints
+    the plain max-abs error beside the error of the exact value rounded to
+    bf16 (the best any bf16 output can do)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if got.size == 0:
+        return 0.0, 0.0
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    import torch
+    e = np.abs(got - ref)
+    best = np.abs(torch.from_numpy(ref).to(torch.bfloat16).double().numpy() - ref).max()
+    excess = float((e - bf16_half_ulp(ref)).max())
+    mx, mean = float(e.max()), float(e.mean())
+    print(f"  [{name}] max_abs={mx:.3e} (exact value rounded to bf16: {best:.3e}) "
+          f"max beyond half an ulp={excess:.3e} mean_abs={mean:.3e} (tol {max_tol:g} + half ulp, mean {mean_tol:g})",
+          flush=True)
+    assert excess <= max_tol, f"{name}: error beyond half a bf16 ulp {excess:.3e} > {max_tol:g}"
+    assert mean <= mean_tol, f"{name}: mean abs error {mean:.3e} > {mean_tol:g}"
+    return mx, mean
 
 
 def check(name, got, ref, max_tol, mean_tol=None):

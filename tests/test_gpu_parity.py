@@ -184,7 +184,8 @@ def test_c3_backward_full_size():
     w = workloads.CONFIGS["c3"]
     print(f"[c3] generating {w.B}x{w.H}x{w.N}x{w.d}", flush=True)
     q, k, v, do = workloads.workload_inputs(w)
-    _bwd_compare("c3", q, k, v, do, w.causal, w.scale, heads=[0, w.B * w.H - 1])
+    # four whole heads, two of each batch entry (flattened index b·H + h)
+    _bwd_compare("c3", q, k, v, do, w.causal, w.scale, heads=[0, 9, w.H, w.B * w.H - 1])
 
 
 def test_backward_is_deterministic():
