@@ -22,6 +22,7 @@ STATUS_NAMES = {
     3: "FA_ERR_UNSUPPORTED",
     4: "FA_ERR_WORKSPACE",
     5: "FA_ERR_HIP",
+    6: "FA_ERR_SCRATCH_TOO_SMALL",
 }
 
 _lib = None
@@ -82,6 +83,11 @@ def _declare(L):
     L.fa_decode_paged_gqa.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
                                       c_float, vp, c_size, vp]
     L.fa_decode_paged_gqa.restype = c_int
+    L.fa_decode_static_scratch_bytes.argtypes = []
+    L.fa_decode_static_scratch_bytes.restype = c_size
+    L.fa_decode_paged_gqa_static.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
+                                             vp, c_float, vp]
+    L.fa_decode_paged_gqa_static.restype = c_int
     L.fa_prefill_paged.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, vp, vp, vp, c_int, c_int, vp, c_int,
                                    vp, vp, vp, c_int, c_float, vp, vp, c_int, c_int, vp]
     L.fa_prefill_paged.restype = c_int

@@ -68,6 +68,8 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim, dtype or page size not supported";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error";
+    case FA_ERR_SCRATCH_TOO_SMALL:
+      return "FA_ERR_SCRATCH_TOO_SMALL: the problem needs more than the library's 16 MiB static scratch";
   }
   return "unknown fa_status";
 }
@@ -242,10 +244,10 @@ size_t fa_decode_workspace_bytes(int num_seqs, int H, int d, int max_blocks_per_
   return fa::decode_workspace_bytes(num_seqs, H, d, max_blocks_per_seq);
 }
 
-static fa_status decode_impl(int num_seqs, int H, int Hkv, int d, int page_size, int num_pages,
-                             int max_blocks_per_seq, const void* q, const void* kv_pool, const int32_t* block_table,
-                             const int32_t* seq_lens, void* o, float* lse, float scale, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+// Checks shared by the decode entry points (everything but the workspace).
+static fa_status decode_check(int num_seqs, int H, int Hkv, int d, int page_size, int num_pages,
+                              int max_blocks_per_seq, const void* q, const void* kv_pool,
+                              const int32_t* block_table, const int32_t* seq_lens, void* o, float scale) {
   if (num_seqs <= 0 || H <= 0 || Hkv <= 0 || d <= 0 || page_size <= 0 || num_pages <= 0 || max_blocks_per_seq <= 0)
     return FA_ERR_BAD_SHAPE;
   if (H % Hkv != 0) return FA_ERR_BAD_SHAPE;
@@ -259,9 +261,19 @@ static fa_status decode_impl(int num_seqs, int H, int Hkv, int d, int page_size,
     return FA_ERR_BAD_SHAPE;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_BAD_SHAPE;
   if (!q || !kv_pool || !block_table || !seq_lens || !o) return FA_ERR_NULL_PTR;
+  return FA_OK;
+}
+
+static fa_status decode_impl(int num_seqs, int H, int Hkv, int d, int page_size, int num_pages,
+                             int max_blocks_per_seq, const void* q, const void* kv_pool, const int32_t* block_table,
+                             const int32_t* seq_lens, void* o, float* lse, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  fa_status st = decode_check(num_seqs, H, Hkv, d, page_size, num_pages, max_blocks_per_seq, q, kv_pool,
+                              block_table, seq_lens, o, scale);
+  if (st != FA_OK) return st;
   if (!workspace || workspace_bytes < fa::decode_workspace_bytes(num_seqs, H, d, max_blocks_per_seq))
     return FA_ERR_WORKSPACE;
-  fa_status st = device_ready();
+  st = device_ready();
   if (st != FA_OK) return st;
   fa::DecodeArgs a{num_seqs, H, Hkv, d, page_size, num_pages, max_blocks_per_seq, q, kv_pool, block_table, seq_lens,
                    o, lse, scale, static_cast<float*>(workspace), (hipStream_t)stream};
@@ -281,6 +293,27 @@ fa_status fa_decode_paged_gqa(int num_seqs, int H, int Hkv, int d, int page_size
                               void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(num_seqs, H, Hkv, d, page_size, num_pages, max_blocks_per_seq, q, kv_pool, block_table,
                      seq_lens, o, lse, scale, workspace, workspace_bytes, stream);
+}
+
+size_t fa_decode_static_scratch_bytes(void) { return fa::kStaticScratchBytes; }
+
+fa_status fa_decode_paged_gqa_static(int num_seqs, int H, int Hkv, int d, int page_size, int num_pages,
+                                     int max_blocks_per_seq, const void* q, const void* kv_pool,
+                                     const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                                     float scale, void* stream) {
+  fa_status st = decode_check(num_seqs, H, Hkv, d, page_size, num_pages, max_blocks_per_seq, q, kv_pool,
+                              block_table, seq_lens, o, scale);
+  if (st != FA_OK) return st;
+  if (fa::decode_workspace_bytes(num_seqs, H, d, max_blocks_per_seq) > fa::kStaticScratchBytes)
+    return FA_ERR_SCRATCH_TOO_SMALL;
+  st = device_ready();
+  if (st != FA_OK) return st;
+  void* scratch = nullptr;
+  st = hip_status(fa::static_scratch(&scratch));
+  if (st != FA_OK) return st;
+  fa::DecodeArgs a{num_seqs, H, Hkv, d, page_size, num_pages, max_blocks_per_seq, q, kv_pool, block_table, seq_lens,
+                   o, lse, scale, static_cast<float*>(scratch), (hipStream_t)stream};
+  return hip_status(fa::launch_decode(a));
 }
 
 }  // extern "C"

@@ -34,10 +34,20 @@
 // m = max m_b, l = Σ 2^(m_b − m) l_b, O = Σ 2^(m_b − m) õ_b / l — the running
 // max / normaliser update of "Flash Attention 是什么" (ai.lansai.wang),
 // 关键术语解析 §4, applied to partial states instead of single blocks.
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
+
+// Device-resident scratch for callers that cannot allocate (the decode
+// partials of fa_decode_paged_gqa_static).  Each GPU the library runs on
+// holds its own copy, zero-filled when the code object loads, until the
+// process ends.  Host code never names this array directly: its name is a
+// host-side stand-in, so kernels get the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -528,6 +538,25 @@ hipError_t launch_gqa(const DecodeArgs& a) {
 }
 
 }  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {  // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a) {
   if (a.Hkv != a.H) return a.d == 128 ? launch_gqa<128>(a) : launch_gqa<64>(a);

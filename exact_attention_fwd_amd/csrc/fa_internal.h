@@ -95,6 +95,11 @@ hipError_t launch_forward(const ForwardArgs& a);
 hipError_t launch_backward(const BackwardArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 
+// Bytes of the per-device static scratch behind fa_decode_paged_gqa_static.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+// Device address of this device's static scratch (looked up once per device).
+hipError_t static_scratch(void** ptr);
+
 // Workspace sizes (bytes, rounded up to 256).
 size_t backward_workspace_bytes(long long rows);  // rows of LSE: B*H*N dense, H*total varlen
 size_t decode_workspace_bytes(long long S, long long H, long long d, long long max_blocks);

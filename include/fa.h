@@ -49,7 +49,8 @@ typedef enum {
   FA_ERR_BAD_SHAPE = 2,    /* a size is negative/zero where it may not be, or overflows */
   FA_ERR_UNSUPPORTED = 3,  /* head dim, dtype or page size this build does not handle  */
   FA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than *_workspace_bytes()       */
-  FA_ERR_HIP = 5           /* the HIP runtime reported an error (no device, launch)    */
+  FA_ERR_HIP = 5,          /* the HIP runtime reported an error (no device, launch)    */
+  FA_ERR_SCRATCH_TOO_SMALL = 6  /* the library's static scratch cannot hold the problem  */
 } fa_status;
 
 typedef enum {
@@ -243,6 +244,31 @@ fa_status fa_decode_paged_gqa(int num_seqs, int H, int Hkv, int d, int page_size
                               const int32_t* block_table, const int32_t* seq_lens,
                               void* o, float* lse, float scale,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_decode_paged_gqa_static — fa_decode_paged_gqa for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument and no allocation
+ * of any kind.  The decode partials go to a static device array of
+ * fa_decode_static_scratch_bytes() bytes (16 MiB) that the library holds on
+ * every GPU it runs on until the process ends; its address is looked up once
+ * per device, on the first call made with that device current.
+ *   Arguments, outputs and results as fa_decode_paged_gqa (Hkv == H is the
+ *   plain paged decode).  A problem whose partials, fa_decode_workspace_bytes(
+ *   num_seqs, H, d, max_blocks_per_seq), exceed the scratch returns
+ *   FA_ERR_SCRATCH_TOO_SMALL before anything is launched.
+ *   Every call on one GPU shares that GPU's scratch: calls that may overlap
+ *   on one GPU (different streams, or different host threads without
+ *   ordering) race and corrupt each other's results.  Nothing in the scratch
+ *   needs to start at zero (every partial that is read is written first in
+ *   the same call).
+ */
+size_t fa_decode_static_scratch_bytes(void);
+fa_status fa_decode_paged_gqa_static(int num_seqs, int H, int Hkv, int d, int page_size,
+                                     int num_pages, int max_blocks_per_seq,
+                                     const void* q, const void* kv_pool,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     void* o, float* lse, float scale, void* stream);
 
 /*
  * fa_prefill_paged — chunked prefill over a paged KV cache: every sequence

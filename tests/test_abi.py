@@ -14,7 +14,7 @@ from exact_attention_fwd_amd import _lib
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fa.h")
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first, or there is no device
 
-OK, NULL, SHAPE, UNSUP, WS, HIP = 0, 1, 2, 3, 4, 5
+OK, NULL, SHAPE, UNSUP, WS, HIP, SCRATCH = 0, 1, 2, 3, 4, 5, 6
 
 
 def declared_functions():
@@ -47,7 +47,7 @@ def test_library_carries_gfx950_code_objects(L):
 
 
 def test_status_strings_and_version(L):
-    for code in range(6):
+    for code in range(7):
         s = L.fa_status_str(code).decode()
         assert s.startswith(_lib.status_name(code))
     assert L.fa_version() >= 10000
@@ -104,6 +104,27 @@ def test_decode_validation(L):
     assert dec(ptr=None) == NULL
     assert dec(ws=None) == WS
     assert dec(wsb=100) == WS
+
+
+def test_static_decode_validation(L):
+    """The allocation-free decode validates like fa_decode_paged_gqa and refuses
+    a problem whose partials exceed its static scratch, before any launch."""
+    assert L.fa_decode_static_scratch_bytes() == 16 << 20
+
+    def dec(S=2, H=8, Hkv=2, d=128, page=256, P=4, mb=2, ptr=FAKE):
+        return L.fa_decode_paged_gqa_static(S, H, Hkv, d, page, P, mb, ptr, ptr, ptr, ptr, ptr, ptr, 0.1, None)
+    assert dec(page=128) == UNSUP
+    assert dec(d=32) == UNSUP
+    assert dec(S=0) == SHAPE
+    assert dec(Hkv=3) == SHAPE
+    assert dec(ptr=None) == NULL
+    # partials: S·H·2·mb·(d+2)·4 bytes; 8 x 32 x 2 x 64 x 130 x 4 = 17 MB > 16 MiB
+    assert L.fa_decode_workspace_bytes(8, 32, 128, 64) > 16 << 20
+    assert dec(S=8, H=32, Hkv=8, mb=64) == SCRATCH
+    assert L.fa_decode_workspace_bytes(8, 32, 128, 63) <= 16 << 20
+    if not torch.cuda.is_available():  # fits: reaches the device check (never launched with fake pointers)
+        assert dec(S=8, H=32, Hkv=8, mb=63) == HIP
+    assert L.fa_status_str(SCRATCH).decode().startswith("FA_ERR_SCRATCH_TOO_SMALL")
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
