@@ -141,24 +141,14 @@ def bench_forward_gqa(steps, warmup, Hkv=8):
             "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-VARLEN_SEED = 1010
-
-
-def varlen_lengths():
-    """16 sequence lengths drawn uniform in [256, 8192] (seeded)."""
-    import torch
-    g = torch.Generator().manual_seed(VARLEN_SEED)
-    return torch.randint(256, 8193, (16,), generator=g).tolist()
-
-
 def bench_varlen(steps, warmup, backward=False):
     """Packed variable-length causal forward (or backward), H=32, d=128."""
     import torch
     import exact_attention_fwd_amd as fa
     import workloads
-    lens = varlen_lengths()
+    lens = workloads.varlen_lengths()
     H, d = 32, 128
-    cu, q, k, v, do = workloads.varlen_inputs(lens, H, H, d, "bf16", seed=VARLEN_SEED, with_dout=True)
+    cu, q, k, v, do = workloads.varlen_inputs(lens, H, H, d, "bf16", seed=workloads.VARLEN_SEED, with_dout=True)
     cu, q, k, v, do = (t.to("cuda:0") for t in (cu, q, k, v, do))
     mx = max(lens)
     o, lse = fa.forward_varlen(q, k, v, cu, mx, causal=True)

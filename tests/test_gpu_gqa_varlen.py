@@ -91,6 +91,40 @@ def test_gqa_forward_16k_full_size():
     check("gqa 16k LSE", np.concatenate(got_l), np.concatenate(ref_l), LSE_MAX)
 
 
+def test_gqa_backward_full_size():
+    """The grouped-head 8K causal backward the bench times ([2, 16 query heads,
+    4 key/value heads, 8192, 128], same seed), at full size in that launch
+    configuration: dK, dV of two whole key/value heads (one per batch entry,
+    each the sum over its four query heads) and dQ of those eight query heads,
+    element by element against the fp64 oracle."""
+    w = workloads.CONFIGS["c3"]
+    Hkv = 4
+    g = w.H // Hkv
+    print(f"[gqa bwd 8k] generating {w.B}x{w.H}q{Hkv}kv x {w.N}x{w.d}", flush=True)
+    q, k, v, do = workloads.gqa_inputs(w.B, w.H, Hkv, w.N, w.d, "bf16", seed=w.seed, with_dout=True)
+    qd, kd, vd, dod = cuda(q, k, v, do)
+    o, lse = fa().forward(qd, kd, vd, causal=True, scale=w.scale)
+    dq, dk, dv = fa().backward(qd, kd, vd, o, dod, lse, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    got = {n: [] for n in ("dq", "dk", "dv")}
+    ref = {n: [] for n in ("dq", "dk", "dv")}
+    for b, j in ((0, 0), (1, Hkv - 1)):
+        rk = np.zeros((w.N, w.d))
+        rv = np.zeros((w.N, w.d))
+        for h in range(j * g, (j + 1) * g):
+            rq, rk_h, rv_h = oracle.attention_backward(q[b, h], k[b, j], v[b, j], do[b, h], causal=True,
+                                                       scale=w.scale)
+            got["dq"].append(to64(dq[b, h]).ravel()), ref["dq"].append(rq.ravel())
+            rk += rk_h
+            rv += rv_h
+        got["dk"].append(to64(dk[b, j]).ravel()), ref["dk"].append(rk.ravel())
+        got["dv"].append(to64(dv[b, j]).ravel()), ref["dv"].append(rv.ravel())
+    check("gqa bwd 8k dq", np.concatenate(got["dq"]), np.concatenate(ref["dq"]), BF16_MAX, BF16_MEAN)
+    check_rounded("gqa bwd 8k dk", np.concatenate(got["dk"]), np.concatenate(ref["dk"]), BF16_MAX, BF16_MEAN)
+    check_rounded("gqa bwd 8k dv", np.concatenate(got["dv"]), np.concatenate(ref["dv"]), BF16_MAX, BF16_MEAN)
+
+
 def test_gqa_forward_fp32():
     q, k, v = workloads.gqa_inputs(1, 4, 2, 77, 64, "f32", seed=5)
     o, lse = fa().forward(*cuda(q, k, v), causal=True)
@@ -148,6 +182,52 @@ def _varlen_compare(lens, H, Hkv, d, causal, dtype="bf16", with_bwd=True, seed=0
 @pytest.mark.parametrize("lens", ["mixed", "one", "tiny", "tiles"])
 def test_varlen_forward_backward(lens, causal, d):
     _varlen_compare(LENS[lens], 4, 2, d, causal, seed=len(LENS[lens]) + d)
+
+
+def test_varlen_full_size():
+    """The packed causal batch the bench times (16 sequences of 527 .. 7723
+    tokens, 80 620 rows, H = 32, d = 128, same seed), forward and backward at
+    full size in that launch configuration.  Forward: two whole (sequence,
+    head) pairs, the longest and the shortest sequence, plus sampled rows of two
+    more; backward: dQ, dK, dV of two whole pairs; all against the fp64 oracle
+    on the sequence cut out of the packed rows."""
+    lens = workloads.varlen_lengths()
+    H, d = 32, 128
+    scale = 1 / math.sqrt(d)
+    print(f"[varlen full] lens={lens} H={H} d={d}", flush=True)
+    cu, q, k, v, do = workloads.varlen_inputs(lens, H, H, d, "bf16", seed=workloads.VARLEN_SEED, with_dout=True)
+    cud, qd, kd, vd, dod = cuda(cu, q, k, v, do)
+    mx = max(lens)
+    o, lse = fa().forward_varlen(qd, kd, vd, cud, mx, causal=True)
+    dq, dk, dv = fa().backward_varlen(qd, kd, vd, o, dod, lse, cud, mx, causal=True)
+    torch.cuda.synchronize()
+    o, lse, dq, dk, dv = (t.cpu() for t in (o, lse, dq, dk, dv))
+    cut = lambda x, s, h: x[int(cu[s]):int(cu[s + 1]), h]  # noqa: E731
+    longest, shortest = int(np.argmax(lens)), int(np.argmin(lens))
+    got_o, ref_o, got_l, ref_l = [], [], [], []
+    for s_, h in ((longest, 0), (shortest, H - 1)):
+        ro, rl = oracle.attention_forward(cut(q, s_, h), cut(k, s_, h), cut(v, s_, h), causal=True, scale=scale)
+        got_o.append(to64(cut(o, s_, h)).ravel()), ref_o.append(ro.ravel())
+        got_l.append(to64(cut(lse.T, s_, h)).ravel()), ref_l.append(rl.ravel())
+    rng = np.random.default_rng(5)
+    for s_, h in ((0, 13), (12, 20)):
+        L = lens[s_]
+        rows = sorted(set([0, 1, 63, 64, L - 65, L - 64, L - 2, L - 1] + rng.integers(0, L, 24).tolist()))
+        ro, rl = oracle.attention_forward_rows(cut(q, s_, h), cut(k, s_, h), cut(v, s_, h), rows, causal=True,
+                                               scale=scale)
+        got_o.append(to64(cut(o, s_, h))[rows].ravel()), ref_o.append(ro.ravel())
+        got_l.append(to64(cut(lse.T, s_, h))[rows].ravel()), ref_l.append(rl.ravel())
+    check("varlen full O", np.concatenate(got_o), np.concatenate(ref_o), BF16_MAX, BF16_MEAN)
+    check("varlen full LSE", np.concatenate(got_l), np.concatenate(ref_l), LSE_MAX)
+    got = {n: [] for n in ("dq", "dk", "dv")}
+    ref = {n: [] for n in ("dq", "dk", "dv")}
+    for s_, h in ((shortest, 5), (longest, 17)):
+        r = oracle.attention_backward(cut(q, s_, h), cut(k, s_, h), cut(v, s_, h), cut(do, s_, h), causal=True,
+                                      scale=scale)
+        for n_, g_, r_ in zip(("dq", "dk", "dv"), (dq, dk, dv), r):
+            got[n_].append(to64(cut(g_, s_, h)).ravel()), ref[n_].append(r_.ravel())
+    for n_ in ("dq", "dk", "dv"):
+        check(f"varlen full {n_}", np.concatenate(got[n_]), np.concatenate(ref[n_]), BF16_MAX, BF16_MEAN)
 
 
 def test_varlen_blocks_ordered_per_kv_head():

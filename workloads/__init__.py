@@ -188,6 +188,14 @@ def gqa_inputs(B, H, Hkv, N, d, dtype="bf16", seed=0, with_dout=False):
     return q, k, v, _draw(g, (B, H, N, d), dtype)
 
 
+VARLEN_SEED = 1010
+
+
+def varlen_lengths(count=16, lo=256, hi=8192, seed=VARLEN_SEED):
+    """The packed-batch length mix: `count` lengths drawn uniform in [lo, hi] (seeded)."""
+    return torch.randint(lo, hi + 1, (count,), generator=_gen(seed)).tolist()
+
+
 def varlen_inputs(lens, H, Hkv, d, dtype="bf16", seed=0, with_dout=False):
     """A packed batch: cu_seqlens int32 [B+1], Q [total, H, d], K/V [total, Hkv, d] (and dO)."""
     g = _gen(seed)
