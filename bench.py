@@ -167,25 +167,13 @@ def bench_varlen(steps, warmup, backward=False):
             "tflops": fl / (avg * 1e-3) / 1e12, "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-PREFILL_SEED = 1020
-
-
-def prefill_shapes():
-    """8 sequences, each a 2048-token chunk appended to a cached prefix drawn
-    uniform in [0, 6144] tokens (seeded)."""
-    import torch
-    g = torch.Generator().manual_seed(PREFILL_SEED)
-    prefix = torch.randint(0, 6145, (8,), generator=g).tolist()
-    return [2048] * 8, [p + 2048 for p in prefix]
-
-
 def bench_prefill(steps, warmup, Hkv=8):
     """Causal chunked prefill through the paged pool, H=32 query heads, d=128."""
     import exact_attention_fwd_amd as fa
     import workloads
-    chunks, ctx = prefill_shapes()
+    chunks, ctx = workloads.prefill_shapes()
     H, d = 32, 128
-    p = workloads.prefill_inputs(chunks, ctx, H=H, Hkv=Hkv, d=d, seed=PREFILL_SEED)
+    p = workloads.prefill_inputs(chunks, ctx, H=H, Hkv=Hkv, d=d, seed=workloads.PREFILL_SEED)
     q, pool, bt, sl, cu = (t.to("cuda:0") for t in (p.q, p.kv_pool, p.block_table, p.seq_lens_k,
                                                     p.cu_seqlens_q))
     o, lse = fa.prefill_paged(q, pool, bt, sl, cu, max(chunks), causal=True)

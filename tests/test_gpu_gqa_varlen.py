@@ -371,6 +371,36 @@ def test_prefill_paged(case, causal, d):
     _prefill_compare(f"prefill {case}", p, causal)
 
 
+def test_prefill_paged_full_size():
+    """The chunked prefill the bench times (8 chunks of 2048 queries on 3875 ..
+    7530 cached keys, 32 query heads on 8 key/value heads, 256-token pages,
+    same seed), at full size in that launch configuration; every query head
+    of two key/value groups of two sequences (the longest and the shortest
+    cache) is compared element by element with the oracle run on that
+    sequence and group alone."""
+    chunks, ctx = workloads.prefill_shapes()
+    H, Hkv, d = 32, 8, 128
+    g = H // Hkv
+    print(f"[prefill full] chunks={chunks} ctx={ctx}", flush=True)
+    p = workloads.prefill_inputs(chunks, ctx, H=H, Hkv=Hkv, d=d, seed=workloads.PREFILL_SEED)
+    qd, pool, bt, sl, cu = cuda(p.q, p.kv_pool, p.block_table, p.seq_lens_k, p.cu_seqlens_q)
+    o, lse = fa().prefill_paged(qd, pool, bt, sl, cu, max(chunks), causal=True)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    cuq = p.cu_seqlens_q.tolist()
+    got_o, ref_o, got_l, ref_l = [], [], [], []
+    for b, j in ((int(np.argmax(ctx)), 0), (int(np.argmin(ctx)), Hkv - 1)):
+        t0, t1 = cuq[b], cuq[b + 1]
+        heads = slice(g * j, g * (j + 1))
+        ro, rl = oracle.prefill_paged(p.q[t0:t1, heads], p.kv_pool[:, :, :, j:j + 1], p.block_table[b:b + 1],
+                                      p.seq_lens_k[b:b + 1], torch.tensor([0, t1 - t0], dtype=torch.int32),
+                                      causal=True, scale=1 / math.sqrt(d), page_size=p.page_size)
+        got_o.append(to64(o[t0:t1, heads]).ravel()), ref_o.append(ro.ravel())
+        got_l.append(to64(lse[heads, t0:t1]).ravel()), ref_l.append(rl.ravel())
+    check("prefill full O", np.concatenate(got_o), np.concatenate(ref_o), BF16_MAX, BF16_MEAN)
+    check("prefill full LSE", np.concatenate(got_l), np.concatenate(ref_l), LSE_MAX)
+
+
 @pytest.mark.parametrize("Hkv", [8, 1])
 def test_prefill_paged_heads(Hkv):
     p = workloads.prefill_inputs([130, 40], [900, 40], H=8, Hkv=Hkv, d=128, seed=Hkv)

@@ -220,6 +220,17 @@ class PrefillInputs:
     page_size: int
 
 
+PREFILL_SEED = 1020
+
+
+def prefill_shapes(count=8, chunk=2048, max_prefix=6144, seed=PREFILL_SEED):
+    """The chunked-prefill mix: `count` sequences, each a `chunk`-token chunk
+    appended to a cached prefix drawn uniform in [0, max_prefix] tokens
+    (seeded); returns (chunk lengths, cached keys per sequence)."""
+    prefix = torch.randint(0, max_prefix + 1, (count,), generator=_gen(seed)).tolist()
+    return [chunk] * count, [p + chunk for p in prefix]
+
+
 def prefill_inputs(chunk_lens, ctx_lens, H=32, Hkv=None, d=128, max_blocks=None, seed=0,
                    page_size=PAGE_SIZE, poison=False, spare_pages=0):
     """A chunked prefill over a paged cache: sequence b has ctx_lens[b] cached
