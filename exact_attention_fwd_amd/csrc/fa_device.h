@@ -305,6 +305,17 @@ __device__ __forceinline__ void mfma_s(f32x16& s, const bf16x8& a, const bf16x8&
 __device__ __forceinline__ void mfma_o(f32x16& o, const bf16x8& a, const bf16x8& p) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(p));
 }
+// The same products pinned in program order (volatile), for software
+// pipelines whose slots are laid out by hand.
+__device__ __forceinline__ void mfma_s0_here(f32x16& s, const bf16x8& a, const bf16x8& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "a"(q));
+}
+__device__ __forceinline__ void mfma_s_here(f32x16& s, const bf16x8& a, const bf16x8& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "a"(q));
+}
+__device__ __forceinline__ void mfma_o_here(f32x16& o, const bf16x8& a, const bf16x8& p) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(p));
+}
 // x *= alpha for a value held in an accumulation register.
 __device__ __forceinline__ void acc_scale(float& x, float alpha) {
   float t;

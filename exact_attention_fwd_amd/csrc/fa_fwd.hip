@@ -44,6 +44,33 @@ __device__ __forceinline__ void max3_here(float& m, float a, float b) {
   asm volatile("v_max3_f32 %0, %0, %1, %2" : "+v"(m) : "v"(a), "v"(b));
 }
 
+// The softmax operations of the w64 forward's software pipeline, each one
+// instruction that stays where it is written (between the products of its
+// pipeline slot).  Every consumer of a result is placed at least one slot
+// (one 32-cycle product) after its producer, so no result is read by the next
+// instruction and no wait states are needed.
+__device__ __forceinline__ void fma_here(float& d, float a, float b, float c) {
+  asm volatile("v_fma_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
+}
+__device__ __forceinline__ void exp2_here(float& d, float a) { asm volatile("v_exp_f32 %0, %1" : "=v"(d) : "v"(a)); }
+__device__ __forceinline__ void add_here(float& d, float a, float b) {
+  asm volatile("v_add_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void accumulate_here(float& d, float a) { asm volatile("v_add_f32 %0, %0, %1" : "+v"(d) : "v"(a)); }
+// lo, hi rounded to bf16 (nearest even) and packed, as pack_bf16x2
+__device__ __forceinline__ void pack_here(uint32_t& d, float lo, float hi) {
+  asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(d) : "v"(lo), "v"(hi));
+}
+
+// Pipeline slot of the fma of score value x (0 .. 63, pair x / 2) of a tile:
+// the 64 values are spread evenly over slots 0 .. SPAN-1; the value's exp
+// issues one slot later, the pair's pack and sum one slot after its second
+// exp, and the running sum one slot after that.
+template <int SPAN>
+constexpr int fma_slot(int x) {
+  return (x * SPAN) / 64;
+}
+
 // Rescale the output only when the running max grows by more than this many
 // powers of two.  Between rescales p = 2^(s·scale·log2e − m) <= 2^8: the
 // output, its normaliser and the logsumexp all use the same reference m, so
@@ -701,9 +728,13 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
   constexpr int NS = 2 * KSTEPS;
   constexpr int NP = 4 * DBLK;
   constexpr int NT = NS + NP;
-  constexpr int SPAN = NS + 3 * DBLK - 2;
-  constexpr int MAX0 = NS + 2;
-  constexpr int MAXN = 2 * NT - 8;   // half-slots 2·MAX0 .. MAXN-1 take the max of S(t+1)
+  // Softmax of S(t): value x's fma in half-slot fma_slot<PSPAN>(x) (the last
+  // pack lands two half-slots before the product that reads it).  Max of
+  // S(t+1): key block 0's values over half-slots MAXA .. MAXB-1, key block 1's
+  // over MAXB .. MAXN-1, each block at least five half-slots after its last
+  // product.
+  constexpr int PSPAN = 54;
+  constexpr int MAXA = 20, MAXB = 36, MAXN = 56;
   constexpr int DEC = 2 * NT - 6;    // half-slots DEC, DEC + 1: its reduction and rescale test
   // The loads of K(t+2) and V(t+1) go out one instruction every other
   // half-slot from DMA0 on: issued in one burst, the four wavefronts' loads
@@ -729,6 +760,11 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
     for (int j = 0; j < 2; ++j) m_use[j] = (m_run[j] == kNegInf) ? 0.f : m_run[j];
     bf16x8 op[LOOK + 1];
     u32x4 pw[2][4];  // P(t) of query block j, keys 16kk .. as packed bf16 pairs
+    float px[32][2];  // score pair pi: s·scale·log2e − m, then its exp
+    float pt[32];     // and the pair's sum
+    float nm[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) nm[j] = -m_use[j];
     float mx[2] = {kNegInf, kNegInf};
     float mt[2];
     uint64_t need[2];
@@ -754,32 +790,39 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
       if constexpr (sl < NS) {
         constexpr int kb = sl / KSTEPS, kk = sl % KSTEPS;
         if constexpr (kk == 0)
-          mfma_s0(sn[2 * kb + j], op[sl % (LOOK + 1)], qreg[j][kk]);
+          mfma_s0_here(sn[2 * kb + j], op[sl % (LOOK + 1)], qreg[j][kk]);
         else
-          mfma_s(sn[2 * kb + j], op[sl % (LOOK + 1)], qreg[j][kk]);
+          mfma_s_here(sn[2 * kb + j], op[sl % (LOOK + 1)], qreg[j][kk]);
       } else {
         constexpr int jj = sl - NS;
         constexpr int kk = jj / DBLK, b = jj % DBLK;
-        mfma_o(oacc[b][j], op[sl % (LOOK + 1)], __builtin_bit_cast(bf16x8, pw[j][kk]));
+        mfma_o_here(oacc[b][j], op[sl % (LOOK + 1)], __builtin_bit_cast(bf16x8, pw[j][kk]));
       }
       // score pairs: pi = 8 kk + 4 jp + w  (kk = key chunk, jp = query block, w = pair inside it)
       static_for<0, 32>([&](auto pic) __attribute__((always_inline)) {
         constexpr int pi = decltype(pic)::value;
-        if constexpr ((pi * SPAN) / 16 == hs) {
-          constexpr int kk = pi / 8, jp = (pi / 4) % 2, w = pi % 4;
-          constexpr int kb = kk / 2, r = 8 * (kk % 2) + 2 * w;
-          const float p0 = exp2_fast(__builtin_fmaf(sc[2 * kb + jp][r], scale_log2, -m_use[jp]));
-          const float p1 = exp2_fast(__builtin_fmaf(sc[2 * kb + jp][r + 1], scale_log2, -m_use[jp]));
-          pw[jp][kk][w] = pack_bf16x2(p0, p1);
-          l_run[jp] += p0 + p1;
+        constexpr int kk = pi / 8, jp = (pi / 4) % 2, w = pi % 4;
+        constexpr int kb = kk / 2, r = 8 * (kk % 2) + 2 * w;
+        constexpr int f0 = fma_slot<PSPAN>(2 * pi), f1 = fma_slot<PSPAN>(2 * pi + 1), pk = f1 + 2;
+        static_assert(pk <= 2 * NS + 8 * kk + jp - 2, "a P chunk must be packed two half-slots before its product");
+        if constexpr (f0 == hs) fma_here(px[pi][0], sc[2 * kb + jp][r], scale_log2, nm[jp]);
+        if constexpr (f1 == hs) fma_here(px[pi][1], sc[2 * kb + jp][r + 1], scale_log2, nm[jp]);
+        if constexpr (f0 + 1 == hs) exp2_here(px[pi][0], px[pi][0]);
+        if constexpr (f1 + 1 == hs) exp2_here(px[pi][1], px[pi][1]);
+        if constexpr (pk == hs) {
+          uint32_t packed;
+          pack_here(packed, px[pi][0], px[pi][1]);
+          pw[jp][kk][w] = packed;
+          add_here(pt[pi], px[pi][0], px[pi][1]);
         }
+        if constexpr (pk + 1 == hs) accumulate_here(l_run[jp], pt[pi]);  // fp32 sum of the unrounded p
       });
       static_for<0, 32>([&](auto vc_) __attribute__((always_inline)) {
         constexpr int v = 2 * decltype(vc_)::value;  // values v, v+1 of S(t+1)
-        if constexpr (2 * MAX0 + (v * (MAXN - 2 * MAX0)) / 64 == hs) {
-          constexpr int blk = v / 16;  // block 2kb + j
-          max3_here(mx[blk % 2], sn[blk][v % 16], sn[blk][v % 16 + 1]);
-        }
+        constexpr int blk = v / 16;                  // block 2kb + j
+        constexpr int at = v < 32 ? MAXA + (v * (MAXB - MAXA)) / 32 : MAXB + ((v - 32) * (MAXN - MAXB)) / 32;
+        static_assert(at < DEC, "the max of S(t+1) precedes its test");
+        if constexpr (at == hs) max3_here(mx[blk % 2], sn[blk][v % 16], sn[blk][v % 16 + 1]);
       });
       if constexpr (hs == DEC || hs == DEC + 1) test(hs - DEC);
       if constexpr (hs >= DMA0 && (hs - DMA0) % 2 == 0 && (hs - DMA0) / 2 < 2 * DMA_PER_WAVE) {
