@@ -316,6 +316,25 @@ __device__ __forceinline__ void mfma_s_here(f32x16& s, const bf16x8& a, const bf
 __device__ __forceinline__ void mfma_o_here(f32x16& o, const bf16x8& a, const bf16x8& p) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(p));
 }
+// Softmax operations for software pipelines laid out by hand (the w64
+// forward), each one instruction that stays where it is
+// written (between the products of its pipeline slot).  The callers place
+// every consumer of a result at least one slot (one 32-cycle product) after
+// its producer, so no result is read by the next instruction and no wait
+// states are needed.
+__device__ __forceinline__ void fma_here(float& d, float a, float b, float c) {
+  asm volatile("v_fma_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
+}
+__device__ __forceinline__ void exp2_here(float& d, float a) { asm volatile("v_exp_f32 %0, %1" : "=v"(d) : "v"(a)); }
+__device__ __forceinline__ void add_here(float& d, float a, float b) {
+  asm volatile("v_add_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void accumulate_here(float& d, float a) { asm volatile("v_add_f32 %0, %0, %1" : "+v"(d) : "v"(a)); }
+// lo, hi rounded to bf16 (nearest even) and packed, as pack_bf16x2
+__device__ __forceinline__ void pack_here(uint32_t& d, float lo, float hi) {
+  asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(d) : "v"(lo), "v"(hi));
+}
+
 // x *= alpha for a value held in an accumulation register.
 __device__ __forceinline__ void acc_scale(float& x, float alpha) {
   float t;

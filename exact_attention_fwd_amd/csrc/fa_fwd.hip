@@ -44,24 +44,6 @@ __device__ __forceinline__ void max3_here(float& m, float a, float b) {
   asm volatile("v_max3_f32 %0, %0, %1, %2" : "+v"(m) : "v"(a), "v"(b));
 }
 
-// The softmax operations of the w64 forward's software pipeline, each one
-// instruction that stays where it is written (between the products of its
-// pipeline slot).  Every consumer of a result is placed at least one slot
-// (one 32-cycle product) after its producer, so no result is read by the next
-// instruction and no wait states are needed.
-__device__ __forceinline__ void fma_here(float& d, float a, float b, float c) {
-  asm volatile("v_fma_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
-}
-__device__ __forceinline__ void exp2_here(float& d, float a) { asm volatile("v_exp_f32 %0, %1" : "=v"(d) : "v"(a)); }
-__device__ __forceinline__ void add_here(float& d, float a, float b) {
-  asm volatile("v_add_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void accumulate_here(float& d, float a) { asm volatile("v_add_f32 %0, %0, %1" : "+v"(d) : "v"(a)); }
-// lo, hi rounded to bf16 (nearest even) and packed, as pack_bf16x2
-__device__ __forceinline__ void pack_here(uint32_t& d, float lo, float hi) {
-  asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(d) : "v"(lo), "v"(hi));
-}
-
 // Pipeline slot of the fma of score value x (0 .. 63, pair x / 2) of a tile:
 // the 64 values are spread evenly over slots 0 .. SPAN-1; the value's exp
 // issues one slot later, the pair's pack and sum one slot after its second
