@@ -83,12 +83,87 @@ def traffic_for(name, per_launch_units=1):
     return rec.get("hbm_bytes_per_launch")
 
 
-def timed_launches(fn, steps, warmup, flush=None):
+# --power SECONDS: after the timed launches, keep launching the path for that
+# long while amd-smi samples board power and clocks (set by main()).
+_POWER = {"seconds": 0.0, "result": None}
+
+
+def power_loop(fn, seconds, idle_s=2.0):
+    """Board power and graphics clocks (amd-smi) while `fn` runs back to back
+    for `seconds`, after `idle_s` of the idle card.  Samples from the first
+    1.5 s of the loop (clock ramp) are left out of the loaded figures."""
+    import subprocess
+    import threading
+    import torch
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            t = time.time()
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                                   timeout=30)
+                j = json.loads(r.stdout)
+                g = j["gpu_data"][0] if isinstance(j, dict) else j[0]
+                clk = [v["clk"]["value"] for k, v in g["clock"].items() if k.startswith("gfx_")]
+                samples.append((t, float(g["power"]["socket_power"]["value"]), clk))
+            except (OSError, ValueError, KeyError, IndexError, TypeError, subprocess.SubprocessError):
+                pass
+            stop.wait(0.2)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    time.sleep(idle_s)
+    t0 = time.time()
+    n = 0
+    while time.time() - t0 < seconds:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        n += 20
+    t1 = time.time()
+    stop.set()
+    th.join(timeout=60)
+    idle = [p for t, p, c in samples if t < t0]
+    load = [(p, c) for t, p, c in samples if t0 + 1.5 <= t <= t1]
+    if not load:
+        return {"tool": "amd-smi metric -p -c --json", "error": "no samples"}
+    clocks = [sum(c) / len(c) for p, c in load if c]
+    return {"tool": "amd-smi metric -p -c --json", "loop_s": round(t1 - t0, 2), "launches": n,
+            "ms_per_launch_wall": round((t1 - t0) * 1e3 / n, 4),
+            "idle_socket_w": round(statistics.median(idle), 1) if idle else None,
+            "loaded_socket_w_mean": round(statistics.mean(p for p, c in load), 1),
+            "loaded_socket_w_min": min(p for p, c in load), "loaded_socket_w_max": max(p for p, c in load),
+            "loaded_gfx_mhz_mean": round(statistics.mean(clocks), 1) if clocks else None,
+            "samples_loaded": len(load)}
+
+
+# Untimed warm-up of each secondary record, in seconds of back-to-back calls
+# (on top of its warm-up steps).  After the card has idled (inputs are built
+# on the host between records), the board's power controller first lets the
+# clocks overshoot and then throttles below its steady state for several
+# milliseconds; a record of a short call timed inside that window measures
+# the controller, not the kernel (the 4K forward: 160-180 us per launch there
+# against 141 us from then on, on one card).  The headline record keeps the
+# exact warm-up step count it is given.
+SECONDARY_WARM_S = 0.25
+
+
+def timed_launches(fn, steps, warmup, flush=None, warm_s=0.0):
     """Per-launch HIP event timings on the current stream; returns (avg_ms, median_ms, total_ms)."""
     import torch
     for _ in range(warmup):
+        if flush is not None:
+            flush()
         fn()
     torch.cuda.synchronize()
+    t_end = time.perf_counter() + warm_s
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            if flush is not None:
+                flush()
+            fn()
+        torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -103,10 +178,12 @@ def timed_launches(fn, steps, warmup, flush=None):
     t1.record()
     torch.cuda.synchronize()
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    if _POWER["seconds"] > 0 and _POWER["result"] is None:
+        _POWER["result"] = power_loop(fn, _POWER["seconds"])
     return sum(per) / len(per), statistics.median(per), t0.elapsed_time(t1)
 
 
-def bench_forward(cfg, steps, warmup):
+def bench_forward(cfg, steps, warmup, warm_s=0.0):
     import torch
     import exact_attention_fwd_amd as fa
     import workloads
@@ -115,7 +192,7 @@ def bench_forward(cfg, steps, warmup):
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
     fn = lambda: fa.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
-    avg, med, total = timed_launches(fn, steps, warmup)
+    avg, med, total = timed_launches(fn, steps, warmup, warm_s=warm_s)
     fl = fwd_flops(w.B, w.H, w.N, w.d, w.causal)
     del q, k, v, o, lse
     return {"workload": w.name, "kernel": fwd_kernel_name(w.d) if w.dtype == "bf16" else "fwd_f32_kernel",
@@ -124,7 +201,7 @@ def bench_forward(cfg, steps, warmup):
             "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-def bench_forward_gqa(steps, warmup, Hkv=8):
+def bench_forward_gqa(steps, warmup, Hkv=8, warm_s=0.0):
     """The 16K causal forward with 32 query heads sharing Hkv key/value heads."""
     import torch
     import exact_attention_fwd_amd as fa
@@ -134,14 +211,14 @@ def bench_forward_gqa(steps, warmup, Hkv=8):
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
     fn = lambda: fa.forward(q, k, v, causal=True, scale=w.scale, out=o, lse=lse)
-    avg, med, total = timed_launches(fn, steps, warmup)
+    avg, med, total = timed_launches(fn, steps, warmup, warm_s=warm_s)
     fl = fwd_flops(w.B, w.H, w.N, w.d, True)
     return {"workload": f"fwd_gqa_causal_1x32q{Hkv}kv_16384x128", "kernel": fwd_kernel_name(128),
             "flops_per_launch": fl, "avg_ms": avg, "median_ms": med, "tflops": fl / (avg * 1e-3) / 1e12,
             "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-def bench_varlen(steps, warmup, backward=False):
+def bench_varlen(steps, warmup, backward=False, warm_s=0.0):
     """Packed variable-length causal forward (or backward), H=32, d=128."""
     import torch
     import exact_attention_fwd_amd as fa
@@ -161,13 +238,13 @@ def bench_varlen(steps, warmup, backward=False):
     else:
         fn = lambda: fa.forward_varlen(q, k, v, cu, mx, causal=True, out=o, lse=lse)
         fl = sum(fwd_flops(1, H, L, d, True) for L in lens)
-    avg, med, total = timed_launches(fn, steps, warmup)
+    avg, med, total = timed_launches(fn, steps, warmup, warm_s=warm_s)
     return {"workload": f"{'bwd' if backward else 'fwd'}_varlen_causal_16seq_h32_d128", "seq_lens": lens,
             "total_tokens": int(sum(lens)), "flops_per_launch": fl, "avg_ms": avg, "median_ms": med,
             "tflops": fl / (avg * 1e-3) / 1e12, "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-def bench_prefill(steps, warmup, Hkv=8):
+def bench_prefill(steps, warmup, Hkv=8, warm_s=0.0):
     """Causal chunked prefill through the paged pool, H=32 query heads, d=128."""
     import exact_attention_fwd_amd as fa
     import workloads
@@ -178,7 +255,7 @@ def bench_prefill(steps, warmup, Hkv=8):
                                                     p.cu_seqlens_q))
     o, lse = fa.prefill_paged(q, pool, bt, sl, cu, max(chunks), causal=True)
     fn = lambda: fa.prefill_paged(q, pool, bt, sl, cu, max(chunks), causal=True, out=o, lse=lse)
-    avg, med, total = timed_launches(fn, steps, warmup)
+    avg, med, total = timed_launches(fn, steps, warmup, warm_s=warm_s)
     # visible (query, key) pairs: query i of a chunk of n over L keys sees i + L - n + 1
     vis = sum(n * (L - n) + n * (n + 1) // 2 for n, L in zip(chunks, ctx))
     fl = 4.0 * d * H * vis
@@ -187,7 +264,7 @@ def bench_prefill(steps, warmup, Hkv=8):
             "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-def bench_backward(steps, warmup):
+def bench_backward(steps, warmup, warm_s=0.0):
     import torch
     import exact_attention_fwd_amd as fa
     import workloads
@@ -197,14 +274,14 @@ def bench_backward(steps, warmup):
     ws = torch.empty(fa.backward_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda:0")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     fn = lambda: fa.backward(q, k, v, o, do, lse, causal=w.causal, scale=w.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
-    avg, med, total = timed_launches(fn, steps, warmup)
+    avg, med, total = timed_launches(fn, steps, warmup, warm_s=warm_s)
     fl = bwd_flops(w.B, w.H, w.N, w.d, w.causal)
     return {"workload": w.name, "kernels": "bwd_delta + bwd_dkdv_pipe + bwd_dq", "flops_per_call": fl, "avg_ms": avg,
             "median_ms": med, "tflops": fl / (avg * 1e-3) / 1e12,
             "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-def bench_backward_gqa(steps, warmup, Hkv=4):
+def bench_backward_gqa(steps, warmup, Hkv=4, warm_s=0.0):
     """The c3 causal backward ([2,16,8192,128]) with the 16 query heads sharing
     Hkv key/value heads (dK/dV summed over each group)."""
     import torch
@@ -217,14 +294,14 @@ def bench_backward_gqa(steps, warmup, Hkv=4):
     ws = torch.empty(fa.backward_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda:0")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     fn = lambda: fa.backward(q, k, v, o, do, lse, causal=True, scale=w.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
-    avg, med, total = timed_launches(fn, steps, warmup)
+    avg, med, total = timed_launches(fn, steps, warmup, warm_s=warm_s)
     fl = bwd_flops(w.B, w.H, w.N, w.d, True)
     return {"workload": f"bwd_gqa_causal_2x16q{Hkv}kv_8192x128", "kernels": "bwd_delta + bwd_dkdv_pipe + bwd_dq",
             "flops_per_call": fl, "avg_ms": avg, "median_ms": med, "tflops": fl / (avg * 1e-3) / 1e12,
             "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-def bench_decode(steps, warmup, Hkv=None):
+def bench_decode(steps, warmup, Hkv=None, warm_s=0.0):
     """Paged decode of the 8-sequence configuration; Hkv < 32 stores that many
     key/value heads in the pool (grouped-query decode)."""
     import torch
@@ -241,7 +318,7 @@ def bench_decode(steps, warmup, Hkv=None):
     # timed call.
     scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
     fn = lambda: fa.decode_paged(q, pool, bt, sl, scale=w.scale, workspace=ws, out=o, lse=lse)
-    avg, med, total = timed_launches(fn, steps, warmup, flush=lambda: scratch.sum())
+    avg, med, total = timed_launches(fn, steps, warmup, flush=lambda: scratch.sum(), warm_s=warm_s)
     nbytes = decode_bytes(p)
     grouped = Hkv is not None and Hkv != w.H
     return {"workload": w.name + (f"_kv{Hkv}" if grouped else ""),
@@ -251,13 +328,13 @@ def bench_decode(steps, warmup, Hkv=None):
             "cache": "1 GiB scratch read before every call (cold K/V)"}
 
 
-def bench_copy(steps, warmup):
+def bench_copy(steps, warmup, warm_s=0.0):
     """A plain 1 GiB device-to-device copy: calibrates the HBM byte counters."""
     import torch
     n = 1 << 30
     src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
     dst = torch.empty_like(src)
-    avg, med, total = timed_launches(lambda: dst.copy_(src), steps, warmup)
+    avg, med, total = timed_launches(lambda: dst.copy_(src), steps, warmup, warm_s=warm_s)
     return {"workload": "copy_1GiB", "bytes_read": n, "bytes_written": n, "avg_ms": avg,
             "gbs": 2 * n / (avg * 1e-3) / 1e9}
 
@@ -321,6 +398,12 @@ def main():
                                        "fwdvarlen", "bwdvarlen", "decodegqa", "prefill", "bwdgqa"], default=None,
                     help="run one path only (for profiler runs); prints its record")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm-s", type=float, default=None, metavar="SECONDS",
+                    help="with --only: untimed seconds of back-to-back calls after the warm-up steps "
+                         f"(default: 0 for fwd, the headline record; {SECONDARY_WARM_S} for the others)")
+    ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
+                    help="with --only: afterwards launch the path back to back for SECONDS while amd-smi "
+                         "samples board power and clocks (decode: without the cache flush)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -333,38 +416,44 @@ def main():
         sys.exit(1)
 
     if args.only:
-        rec = {"fwd": lambda: bench_forward("c2a", args.steps, args.warmup),
-               "fwd32k": lambda: bench_forward("c2b", args.steps, args.warmup),
-               "fwdnc": lambda: bench_forward("c2c", args.steps, args.warmup),
-               "fwd4k": lambda: bench_forward("c1", args.steps, args.warmup),
-               "bwd": lambda: bench_backward(args.steps, args.warmup),
-               "copy": lambda: bench_copy(args.steps, args.warmup),
-               "decode": lambda: bench_decode(args.steps, args.warmup),
-               "fwdgqa": lambda: bench_forward_gqa(args.steps, args.warmup),
-               "fwdvarlen": lambda: bench_varlen(args.steps, args.warmup),
-               "bwdvarlen": lambda: bench_varlen(args.steps, args.warmup, backward=True),
-               "decodegqa": lambda: bench_decode(args.steps, args.warmup, Hkv=8),
-               "prefill": lambda: bench_prefill(args.steps, args.warmup),
-               "bwdgqa": lambda: bench_backward_gqa(args.steps, args.warmup)}[args.only]()
+        _POWER["seconds"] = args.power
+        ws = args.warm_s if args.warm_s is not None else (0.0 if args.only == "fwd" else SECONDARY_WARM_S)
+        rec = {"fwd": lambda: bench_forward("c2a", args.steps, args.warmup, warm_s=ws),
+               "fwd32k": lambda: bench_forward("c2b", args.steps, args.warmup, warm_s=ws),
+               "fwdnc": lambda: bench_forward("c2c", args.steps, args.warmup, warm_s=ws),
+               "fwd4k": lambda: bench_forward("c1", args.steps, args.warmup, warm_s=ws),
+               "bwd": lambda: bench_backward(args.steps, args.warmup, warm_s=ws),
+               "copy": lambda: bench_copy(args.steps, args.warmup, warm_s=ws),
+               "decode": lambda: bench_decode(args.steps, args.warmup, warm_s=ws),
+               "fwdgqa": lambda: bench_forward_gqa(args.steps, args.warmup, warm_s=ws),
+               "fwdvarlen": lambda: bench_varlen(args.steps, args.warmup, warm_s=ws),
+               "bwdvarlen": lambda: bench_varlen(args.steps, args.warmup, backward=True, warm_s=ws),
+               "decodegqa": lambda: bench_decode(args.steps, args.warmup, Hkv=8, warm_s=ws),
+               "prefill": lambda: bench_prefill(args.steps, args.warmup, warm_s=ws),
+               "bwdgqa": lambda: bench_backward_gqa(args.steps, args.warmup, warm_s=ws)}[args.only]()
+        rec["warm_s"] = ws
+        if _POWER["result"] is not None:
+            rec["power"] = _POWER["result"]
         print(json.dumps(rec), flush=True)
         return
 
     print("# forward c2a (headline)", file=sys.stderr, flush=True)
     main_rec = bench_forward("c2a", args.steps, args.warmup)
     secondary = []
-    for name, f in (("fwd c1", lambda: bench_forward("c1", args.steps, args.warmup)),
-                    ("fwd c2b", lambda: bench_forward("c2b", max(5, args.steps // 2), 2)),
-                    ("fwd c2c", lambda: bench_forward("c2c", max(5, args.steps // 2), 2)),
-                    ("bwd c3", lambda: bench_backward(max(5, args.steps // 2), 2)),
-                    ("decode c4", lambda: bench_decode(args.steps, args.warmup)),
-                    ("fwd gqa 32q/8kv", lambda: bench_forward_gqa(max(5, args.steps // 2), 2)),
-                    ("bwd gqa 16q/4kv", lambda: bench_backward_gqa(max(5, args.steps // 2), 2)),
-                    ("fwd varlen", lambda: bench_varlen(max(5, args.steps // 2), 2)),
-                    ("bwd varlen", lambda: bench_varlen(max(5, args.steps // 2), 2, backward=True)),
-                    ("decode c4 gqa 32q/8kv", lambda: bench_decode(args.steps, args.warmup, Hkv=8)),
-                    ("prefill paged", lambda: bench_prefill(max(5, args.steps // 2), 2))):
+    ws = SECONDARY_WARM_S
+    for name, f in (("fwd c1", lambda: bench_forward("c1", args.steps, args.warmup, warm_s=ws)),
+                    ("fwd c2b", lambda: bench_forward("c2b", max(5, args.steps // 2), 2, warm_s=ws)),
+                    ("fwd c2c", lambda: bench_forward("c2c", max(5, args.steps // 2), 2, warm_s=ws)),
+                    ("bwd c3", lambda: bench_backward(max(5, args.steps // 2), 2, warm_s=ws)),
+                    ("decode c4", lambda: bench_decode(args.steps, args.warmup, warm_s=ws)),
+                    ("fwd gqa 32q/8kv", lambda: bench_forward_gqa(max(5, args.steps // 2), 2, warm_s=ws)),
+                    ("bwd gqa 16q/4kv", lambda: bench_backward_gqa(max(5, args.steps // 2), 2, warm_s=ws)),
+                    ("fwd varlen", lambda: bench_varlen(max(5, args.steps // 2), 2, warm_s=ws)),
+                    ("bwd varlen", lambda: bench_varlen(max(5, args.steps // 2), 2, backward=True, warm_s=ws)),
+                    ("decode c4 gqa 32q/8kv", lambda: bench_decode(args.steps, args.warmup, Hkv=8, warm_s=ws)),
+                    ("prefill paged", lambda: bench_prefill(max(5, args.steps // 2), 2, warm_s=ws))):
         print(f"# {name}", file=sys.stderr, flush=True)
-        secondary.append(f())
+        secondary.append(dict(f(), warm_s=ws))
         torch.cuda.empty_cache()
     base = None
     if not args.no_cpu_baseline:
