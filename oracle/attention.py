@@ -94,9 +94,11 @@ def _softmax_rows(s: np.ndarray):
     return p, lse
 
 
-def _dscores(p: np.ndarray, dp: np.ndarray) -> np.ndarray:
-    """dS = P ∘ (dP − D) with D_i = sum_j P_ij dP_ij (softmax Jacobian applied row-wise)."""
-    D = (p * dp).sum(axis=1)
+def _dscores(p: np.ndarray, dp: np.ndarray, D: np.ndarray | None = None) -> np.ndarray:
+    """dS = P ∘ (dP − D) with D_i = sum_j P_ij dP_ij (softmax Jacobian applied
+    row-wise), or the given D."""
+    if D is None:
+        D = (p * dp).sum(axis=1)
     return p * (dp - D[:, None])
 
 
@@ -157,15 +159,22 @@ def attention_forward_rows(q, k, v, rows, causal=False, scale=None):
     return _forward_head(q, k, v, causal, scale, rows=np.asarray(rows))
 
 
-def attention_backward(q, k, v, dout, causal=False, scale=None, row_block=1024):
+def attention_backward(q, k, v, dout, causal=False, scale=None, row_block=1024, out=None):
     """dQ, dK, dV of L = sum(O * dO) for inputs of shape [..., N, d].
 
     With P the softmax probabilities of the forward:
       dV = Pᵀ dO;  dP = dO Vᵀ;  D_i = sum_j P_ij dP_ij;
       dS = P ∘ (dP − D);  dQ = scale · dS K;  dK = scale · dSᵀ Q.
+    Since O_i = sum_j P_ij V_j, D_i equals sum_d dO_id O_id.  With `out` (the
+    forward's output as the caller kept it, e.g. rounded to bf16) D is taken
+    as sum_d dO_id out_id instead: the backward of a method that saves O.
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
     _check(q, k, v, causal)
+    if out is not None:
+        out = _f64(out)
+        assert out.shape == q.shape[:-1] + (v.shape[-1],)
+        Dall = (do * out).sum(axis=-1).reshape(-1, q.shape[-2])
     if scale is None:
         scale = 1.0 / np.sqrt(q.shape[-1])
     heads = int(np.prod(q.shape[:-2]))
@@ -181,7 +190,7 @@ def attention_backward(q, k, v, dout, causal=False, scale=None, row_block=1024):
             p, _ = _softmax_rows(s)
             dv[h] += p.T @ dof[h, r]
             dp = dof[h, r] @ vf[h].T
-            ds = _dscores(p, dp)
+            ds = _dscores(p, dp, None if out is None else Dall[h, r])
             dq[h, r] = scale * (ds @ kf[h])
             dk[h] += scale * (ds.T @ qf[h, r])
     return dq.reshape(q.shape), dk.reshape(k.shape), dv.reshape(v.shape)

@@ -313,6 +313,19 @@ def test_decode_gqa_page_splits(d):
     _decode_compare(f"decode pages H=16 Hkv=4 d={d}", p)
 
 
+@pytest.mark.parametrize("H,Hkv,d,max_blocks", [(16, 4, 64, 12), (32, 8, 128, 32)])
+def test_decode_gqa_drifting_scores(H, Hkv, d, max_blocks):
+    """Grouped-head decode on scores that grow along every sequence (drift as
+    in drifting_inputs): the per-tile rescale inside each split and the merge
+    of splits whose maxima lie far apart, with half-page splits (a small block
+    table) and whole-page splits (8 sequences x 32 pages x 8 key/value heads)."""
+    lens = [1, 257, 700, 3000] if max_blocks == 12 else [1, 255, 256, 257, 700, 3000, 6001, 8191]
+    p = workloads.paged_inputs(num_seqs=len(lens), H=H, Hkv=Hkv, d=d, max_blocks=max_blocks, seed=70 + d,
+                               seq_lens=lens, poison=True, spare_pages=2, drift=16.0)
+    print(f"[decode gqa drift] H={H} Hkv={Hkv} d={d} max_blocks={max_blocks}", flush=True)
+    _decode_compare(f"decode drift H={H} Hkv={Hkv} d={d}", p)
+
+
 def test_decode_gqa_is_deterministic():
     p = workloads.paged_inputs(num_seqs=4, H=32, Hkv=8, d=128, len_lo=300, len_hi=3000, max_blocks=12, seed=4)
     args = cuda(p.q, p.kv_pool, p.block_table, p.seq_lens)

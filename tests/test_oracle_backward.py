@@ -78,3 +78,36 @@ def test_conservation(rng, causal):
     np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-12)
     if causal:
         np.testing.assert_allclose(dq[0], 0.0, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_saved_output_path(rng, causal):
+    """The `out` form of the backward (D_i = sum_d dO_id out_id): with the exact
+    forward output it equals the default form (D_i = sum_j P_ij dP_ij, the same
+    number since O_i = sum_j P_ij V_j); with one entry of one output row moved by
+    eps, the gradients move by the closed form of dS changing by -P_ij·dO_ic·eps
+    in row i alone: dQ_i by -scale·dO_ic·eps·sum_j P_ij K_j, dK_j by
+    -scale·dO_ic·eps·P_ij·Q_i, dV not at all."""
+    n, d, scale, eps = 11, 6, 0.7, 1e-3
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    o, _ = attention_forward(q, k, v, causal=causal, scale=scale)
+    base = attention_backward(q, k, v, do, causal=causal, scale=scale)
+    same = attention_backward(q, k, v, do, causal=causal, scale=scale, out=o)
+    for a, b in zip(base, same):
+        np.testing.assert_allclose(b, a, rtol=0, atol=1e-12)
+    i, c = 7, 2
+    o2 = o.copy()
+    o2[i, c] += eps
+    dq2, dk2, dv2 = attention_backward(q, k, v, do, causal=causal, scale=scale, out=o2)
+    s = scale * (q @ k.T)
+    if causal:
+        s = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    dD = do[i, c] * eps
+    want_dq = base[0].copy()
+    want_dq[i] -= scale * dD * (p[i] @ k)
+    want_dk = base[1] - scale * dD * p[i][:, None] * q[i][None, :]
+    np.testing.assert_allclose(dq2, want_dq, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk2, want_dk, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv2, base[2], rtol=0, atol=1e-14)

@@ -47,8 +47,8 @@ MUTATIONS = {
                                                            s.max(1) + np.log(np.exp(s - s.max(1, keepdims=True)).sum(1)))),
     "lse without max": ("_softmax_rows", lambda s: (np.exp(s - s.max(1, keepdims=True)) / np.exp(s - s.max(1, keepdims=True)).sum(1, keepdims=True),
                                                     np.log(np.exp(s - s.max(1, keepdims=True)).sum(1)))),
-    "dS sign flipped": ("_dscores", lambda p, dp: -p * (dp - (p * dp).sum(1, keepdims=True))),
-    "dS drops D": ("_dscores", lambda p, dp: p * dp),
+    "dS sign flipped": ("_dscores", lambda p, dp, D=None: -p * (dp - ((p * dp).sum(1) if D is None else D)[:, None])),
+    "dS drops D": ("_dscores", lambda p, dp, D=None: p * dp),
 }
 
 

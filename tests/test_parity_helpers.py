@@ -29,3 +29,18 @@ def test_check_rounded_accepts_the_rounded_exact_value_and_rejects_more(rng):
         pass
     else:
         raise AssertionError("an error of 5e-2 beyond half an ulp was accepted")
+
+
+def test_rounding_variance_matches_bf16_rounding(rng):
+    """bf16_rounding_var: the variance of the RNE rounding error, binade by
+    binade (ulp^2 / 12), against the error of torch's own rounding of many
+    values spread uniformly inside one binade, and exactly 0 at 0."""
+    from tests.parity import bf16_rounding_var
+    for e in (-12, -1, 0, 3):
+        x = np.exp2(e) * (1.0 + rng.uniform(0.0, 1.0, 200000))
+        err = torch.from_numpy(x).to(torch.bfloat16).double().numpy() - x
+        want = bf16_rounding_var(x)
+        assert np.allclose(want, want[0])               # one binade: one ulp
+        assert want[0] == 2.0 ** (2 * (e - 7)) / 12.0
+        assert abs(err.var() / want[0] - 1.0) < 0.02
+    assert bf16_rounding_var(np.array([0.0]))[0] == 0.0

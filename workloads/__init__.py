@@ -120,7 +120,7 @@ class PagedInputs:
 
 def paged_inputs(num_seqs=8, H=32, d=128, len_lo=1024, len_hi=8192, max_blocks=32,
                  seed=0, page_size=PAGE_SIZE, poison=False, spare_pages=0,
-                 seq_lens=None, Hkv=None):
+                 seq_lens=None, Hkv=None, drift=0.0):
     """Draw a paged KV cache (pool [P, 2, page, Hkv, d], Hkv = H unless given).
 
     Lengths are uniform integers in [len_lo, len_hi] (or given); each sequence
@@ -129,7 +129,10 @@ def paged_inputs(num_seqs=8, H=32, d=128, len_lo=1024, len_hi=8192, max_blocks=3
     entries hold -1.  With ``poison`` the slots past each sequence's length in
     its last page are overwritten with a huge finite key and NaN values, and
     ``spare_pages`` extra pages (never referenced by any table) hold NaN, so a
-    kernel that reads past a sequence's length cannot pass.
+    kernel that reads past a sequence's length cannot pass.  With ``drift``
+    > 0 the scores grow along each sequence as in drifting_inputs: every query
+    gets + sqrt(d)·u and the key at logical position j of a sequence of length
+    L gets + drift·(j / L)·sqrt(d)·u, u one random unit direction.
     """
     g = _gen(seed)
     if seq_lens is None:
@@ -150,6 +153,17 @@ def paged_inputs(num_seqs=8, H=32, d=128, len_lo=1024, len_hi=8192, max_blocks=3
     for s, p in enumerate(pages):
         table[s, :p] = perm[off:off + p].to(torch.int32)
         off += p
+    if drift > 0:
+        u = torch.randn(d, generator=g, dtype=torch.float32)
+        u = u / u.norm()
+        q = (q.float() + math.sqrt(d) * u).to(torch.bfloat16)
+        for s, L in enumerate(lens.tolist()):
+            for b in range(pages[s]):
+                n = min(page_size, L - b * page_size)
+                j = b * page_size + torch.arange(n, dtype=torch.float32)
+                rows = pool[int(table[s, b]), 0, :n].float()  # [n, Hkv, d]
+                rows += (drift * j / L * math.sqrt(d))[:, None, None] * u
+                pool[int(table[s, b]), 0, :n] = rows.to(torch.bfloat16)
     if poison:
         for s, L in enumerate(lens.tolist()):
             last = int(table[s, pages[s] - 1])
