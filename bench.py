@@ -3,6 +3,8 @@
 
 A step is one fused causal forward over [B=1, H=32, N=16384, d=128] bf16 (the
 pages' 16K-token example), inputs resident in HBM before the timed region.
+The headline runs exactly the given warm-up steps; each other record also
+warms up for 0.25 s of back-to-back calls.
 value = algorithmic attention TFLOP/s = 4·d·pairs·B·H / time, pairs = N(N+1)/2.
 The same JSON line also carries the other configurations of the hot path
 (32K and non-causal forward, the recomputing backward, paged decode in GB/s),
@@ -183,12 +185,12 @@ def timed_launches(fn, steps, warmup, flush=None, warm_s=0.0):
     return sum(per) / len(per), statistics.median(per), t0.elapsed_time(t1)
 
 
-def bench_forward(cfg, steps, warmup, warm_s=0.0):
+def bench_forward(cfg, steps, warmup, warm_s=0.0, inputs=None):
     import torch
     import exact_attention_fwd_amd as fa
     import workloads
     w = workloads.CONFIGS[cfg]
-    q, k, v = (t.to("cuda:0") for t in workloads.workload_inputs(w))
+    q, k, v = inputs if inputs is not None else (t.to("cuda:0") for t in workloads.workload_inputs(w))
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
     fn = lambda: fa.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
@@ -400,7 +402,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm-s", type=float, default=None, metavar="SECONDS",
                     help="with --only: untimed seconds of back-to-back calls after the warm-up steps "
-                         f"(default: 0 for fwd, the headline record; {SECONDARY_WARM_S} for the others)")
+                         f"(default {SECONDARY_WARM_S}: a working card, as the full run times every record)")
     ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
                     help="with --only: afterwards launch the path back to back for SECONDS while amd-smi "
                          "samples board power and clocks (decode: without the cache flush)")
@@ -417,7 +419,7 @@ def main():
 
     if args.only:
         _POWER["seconds"] = args.power
-        ws = args.warm_s if args.warm_s is not None else (0.0 if args.only == "fwd" else SECONDARY_WARM_S)
+        ws = args.warm_s if args.warm_s is not None else SECONDARY_WARM_S
         rec = {"fwd": lambda: bench_forward("c2a", args.steps, args.warmup, warm_s=ws),
                "fwd32k": lambda: bench_forward("c2b", args.steps, args.warmup, warm_s=ws),
                "fwdnc": lambda: bench_forward("c2c", args.steps, args.warmup, warm_s=ws),

@@ -316,6 +316,22 @@ __device__ __forceinline__ void mfma_s_here(f32x16& s, const bf16x8& a, const bf
 __device__ __forceinline__ void mfma_o_here(f32x16& o, const bf16x8& a, const bf16x8& p) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(p));
 }
+// The same on 16x16x32 products (result: 4 registers per lane).
+__device__ __forceinline__ void mfma16_s0(f32x4& s, const bf16x8& a, const bf16x8& q) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "a"(q));
+}
+__device__ __forceinline__ void mfma16_s(f32x4& s, const bf16x8& a, const bf16x8& q) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "a"(q));
+}
+__device__ __forceinline__ void mfma16_s0_here(f32x4& s, const bf16x8& a, const bf16x8& q) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "a"(q));
+}
+__device__ __forceinline__ void mfma16_s_here(f32x4& s, const bf16x8& a, const bf16x8& q) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "a"(q));
+}
+__device__ __forceinline__ void mfma16_o_here(f32x4& o, const bf16x8& a, const bf16x8& p) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(p));
+}
 // Softmax operations for software pipelines laid out by hand (the w64
 // forward), each one instruction that stays where it is
 // written (between the products of its pipeline slot).  The callers place
@@ -324,6 +340,10 @@ __device__ __forceinline__ void mfma_o_here(f32x16& o, const bf16x8& a, const bf
 // states are needed.
 __device__ __forceinline__ void fma_here(float& d, float a, float b, float c) {
   asm volatile("v_fma_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
+}
+// d = a·b − c (c negated by the instruction's source modifier).
+__device__ __forceinline__ void fms_here(float& d, float a, float b, float c) {
+  asm volatile("v_fma_f32 %0, %1, %2, -%3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
 }
 __device__ __forceinline__ void exp2_here(float& d, float a) { asm volatile("v_exp_f32 %0, %1" : "=v"(d) : "v"(a)); }
 __device__ __forceinline__ void add_here(float& d, float a, float b) {

@@ -508,33 +508,50 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 // The same forward with 64 queries per wavefront, for d = 128 with K/V laid
 // out like the queries (dense, grouped heads, packed batches) or read
 // through a page table (paged prefill): four wavefronts per workgroup, one
-// per SIMD.  Each K and Vᵀ operand read from
-// LDS feeds two products (query blocks j = 0, 1), halving LDS traffic per
-// FLOP; the output accumulators live in accumulation registers.
+// per SIMD, on 16x16x32 products.  Under the board's power limit a
+// 16x16x32 product costs less energy per FLOP than a 32x32x16 one (it reads
+// and writes a quarter of the accumulator registers for half the work), so
+// the clock the limit allows is higher.  Each K and Vᵀ operand read from LDS
+// feeds four products (query blocks j = 0..3); the output accumulators and
+// Qᵀ live in accumulation registers.
+//
+// Register layout of a 16x16x32 product (lane l, G = l / 16, i = l % 16):
+// the A operand holds row i, k = 8G .. 8G+7; the B operand column i, the
+// same k; the result holds column i, rows 4G .. 4G+3.  Sᵀ block (kb, j) is
+// keys 16kb.. (rows) by queries 16j.. (columns): lane l holds query
+// qw + 16j + i against keys 16kb + 4G + r, r = 0..3.  Those four keys of
+// blocks 2c and 2c+1 are the eight k-values of the Pᵀ operand of key chunk
+// c (32 keys), and the Vᵀ operand reads the same eight keys (4G.. and
+// 16 + 4G.. of the chunk) with two transposed reads, so P needs no shuffle.
 template <bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                                          const bf16* __restrict__ V, bf16* __restrict__ O,
                                                          float* __restrict__ LSE, AttnShape shape, PagedKV pkv,
                                                          float scale_log2) {
   constexpr int D = 128;
-  constexpr int KSTEPS = D / 16;
-  constexpr int DBLK = D / 32;
+  constexpr int KC = D / 32;   // 32-feature k-steps of Sᵀ = K·Qᵀ
+  constexpr int QB = 4;        // 16-query blocks of a wavefront
+  constexpr int KB = 4;        // 16-key blocks of a tile
+  constexpr int DB = D / 16;   // 16-feature blocks of Oᵀ
   constexpr int TILE = kTileRows * D;
   constexpr int CPR = D / 8;
   constexpr int WAVES = 4;
   constexpr int THREADS = 64 * WAVES;
   constexpr int ROWS_PER_DMA = 64 / CPR;
   constexpr int DMA_PER_WAVE = kTileRows / ROWS_PER_DMA / WAVES;
+  static_assert(ROWS_PER_DMA == 4 && DMA_PER_WAVE == 4, "tile loads: 4 rows per load, 4 loads per wavefront");
   __shared__ __attribute__((aligned(1024))) bf16 kbuf0[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 kbuf1[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 vbuf0[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 vbuf1[TILE];
   __shared__ int ptab[PAGED ? kMaxPrefillPages : 1];  // this sequence's pool pages
+  __shared__ __attribute__((aligned(16))) float rsc[THREADS * 4];  // 16 bytes per lane: output rescale staging
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5, n = lane & 31;
+  const int G = lane >> 4, i16 = lane & 15;
+  auto* rsc_lane = (__attribute__((address_space(3))) float*)(rsc + 4 * tid);
   int rank, bi, hi;
   if (PAGED || shape.cu != nullptr)
     map_unit_kv(blockIdx.x, shape.B, shape.H, shape.H / shape.Hkv, rank, bi, hi);
@@ -576,94 +593,100 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
   };
   // Byte offset of tile t inside tile_rsrc(t, ·).
   auto tile_base = [&](int t) { return PAGED ? 0u : (uint32_t)t * (uint32_t)(64 * kvs * 2); };
-  const int qw = q0 + wave * 64;  // this wave's first query; query block j holds qw + 32j ..
+  const int qw = q0 + wave * 64;  // this wave's first query; query block j holds qw + 16j ..
 
-  // Qᵀ as the B operand of both query blocks (zeros past N).
-  bf16x8 qreg[2][KSTEPS];
+  // Qᵀ as the B operand of every query block (zeros past N).
+  bf16x8 qreg[QB][KC];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < QB; ++j)
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk)
+    for (int kk = 0; kk < KC; ++kk)
       qreg[j][kk] = __builtin_bit_cast(
-          bf16x8, buf_load16(rq, (uint32_t)(qw + 32 * j + n) * (hv.qs * 2) + (16 * kk + 8 * g) * 2));
+          bf16x8, buf_load16(rq, (uint32_t)(qw + 16 * j + i16) * (hv.qs * 2) + (32 * kk + 8 * G) * 2));
 
-  // Direct-to-LDS loads: rows (wave·DMA_PER_WAVE + i)·ROWS_PER_DMA + lane / CPR
-  // of a tile; the swizzled chunk offsets are recomputed at each issue.
-  const int dma_row = lane / CPR, dma_pc = lane % CPR;
-  auto dma_off = [&](int i, bool vtile) {
-    const int row = (wave * DMA_PER_WAVE + i) * ROWS_PER_DMA + dma_row;
-    return (uint32_t)row * (kvs * 2) + ((dma_pc ^ (vtile ? v_swz<D>(row) : rm_swz<D>(row))) << 4);
-  };
-  // Spread issue (one load at a time inside the slots): row r = 16·wave + 4i + dma_row,
-  // so the V chunk swizzle (a function of r % 4) is the same for every i and
-  // the K one is (dma_pc ^ dma_row) ^ (8(i & 1) + 4(i >> 1)); the row offset's
-  // i- and tile-dependent part is uniform.  `tbase` is the tile's byte offset,
-  // or an offset past every buffer for a load that is not needed (it then
-  // reads nothing and writes only a slot no one reads again).
-  const uint32_t drow = (uint32_t)(16 * wave + dma_row) * (uint32_t)(kvs * 2);
-  const uint32_t kch = (uint32_t)(dma_pc ^ dma_row) << 4;
-  const uint32_t vlane = drow + ((uint32_t)(dma_pc ^ v_swz<D>(dma_row)) << 4);
+  // Tile layout in LDS: row r of a tile at r·D; its 16-byte chunk c at
+  // position c ^ (r % 16) (K) or c ^ (2r % 16) (V).  A K operand read (16
+  // lanes: 16 rows, one chunk each) then covers all 16 chunk positions, and a
+  // transposed V read (32 lanes: 8 consecutive rows x 2 chunks) 16 distinct
+  // positions, so neither pattern has bank conflicts.  Direct-to-LDS loads
+  // write lane l's 16 bytes at position l % 16 of row l / 16 of their
+  // 4-row block, so each lane fetches the chunk that belongs there:
+  // row r = 16·wave + 4i + G fetches chunk i16 ^ swizzle(r).
+  const uint32_t drow = (uint32_t)(16 * wave + G) * (uint32_t)(kvs * 2);
   auto issue_k1 = [&](bf16* slot, __amdgpu_buffer_rsrc_t r, uint32_t tbase, int i) {
-    const uint32_t ch = kch ^ ((uint32_t)(8 * (i & 1) + 4 * (i >> 1)) << 4);
+    const uint32_t ch = (uint32_t)(i16 ^ ((4 * i + G) & 15)) << 4;
     lds_dma16(r, slot + (wave * DMA_PER_WAVE + i) * 512, drow + ch + (tbase + (uint32_t)(4 * i * kvs * 2)));
   };
   auto issue_v1 = [&](bf16* slot, __amdgpu_buffer_rsrc_t r, uint32_t tbase, int i) {
-    lds_dma16(r, slot + (wave * DMA_PER_WAVE + i) * 512, vlane + (tbase + (uint32_t)(4 * i * kvs * 2)));
+    const uint32_t ch = (uint32_t)(i16 ^ ((8 * i + 2 * G) & 15)) << 4;
+    lds_dma16(r, slot + (wave * DMA_PER_WAVE + i) * 512, drow + ch + (tbase + (uint32_t)(4 * i * kvs * 2)));
   };
   auto issue_k = [&](bf16* slot, int t) {
     const auto r = tile_rsrc(t, 0);
 #pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i)
-      lds_dma16(r, slot + (wave * DMA_PER_WAVE + i) * 512, dma_off(i, false) + tile_base(t));
+    for (int i = 0; i < DMA_PER_WAVE; ++i) issue_k1(slot, r, tile_base(t), i);
   };
   auto issue_v = [&](bf16* slot, int t) {
     const auto r = tile_rsrc(t, 1);
 #pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i)
-      lds_dma16(r, slot + (wave * DMA_PER_WAVE + i) * 512, dma_off(i, true) + tile_base(t));
+    for (int i = 0; i < DMA_PER_WAVE; ++i) issue_v1(slot, r, tile_base(t), i);
   };
 
-  // LDS operand offsets (elements).  K: rows perm_row(n), 16-byte chunk
-  // (2kk + g) ^ (n % 16) = 2(kk ^ c1) + (g ^ c0) with c = n % 16: one base and
-  // an XOR per k-step.  Vᵀ: chunk (4b + x) ^ v_swz(row) with x < 4 is
-  // 4(b ^ s2) + (x ^ (v_swz & 3)), s2 = v_swz >> 2: one base and an XOR per d block.
-  const int kc = n & (CPR - 1);
-  const int kbase = perm_row(n) * D + ((g ^ (kc & 1)) << 3);
-  const int kx = (kc >> 1) << 4;
-  auto koff = [&](int kk) { return kbase + ((kk << 4) ^ kx); };
-  const int G = lane >> 4, j16 = lane & 15;
-  const int vrow = 8 * (G >> 1) + (j16 >> 2);
-  const int vsw = v_swz<D>(vrow);
-  const int vx = 2 * (G & 1) + ((4 * (j16 & 3)) >> 3);
-  const int vbase = vrow * D + ((vx ^ (vsw & 3)) << 3) + ((4 * (j16 & 3)) & 7);
-  const int vs2 = (vsw >> 2) << 5;
-  auto voff = [&](int b) { return vbase + ((b << 5) ^ vs2); };
+  // LDS operand offsets (elements).  K block kb, k-step kk: row 16kb + i16,
+  // chunk 4kk + G at position (4kk + G) ^ i16 = 4kk ^ (G ^ i16).  Vᵀ block db,
+  // key chunk c, half h: lanes address row 32c + 16h + vr (vr = 4G + i16/4),
+  // columns 16db + 4(i16 % 4).. (chunk 2db + (i16 % 4)/2, at position
+  // (2db + x) ^ 2(vr % 8) = 2(db ^ (vr % 8)) + x).
+  const int kbase = i16 * D;
+  const int kx = (G ^ i16) << 3;
+  auto koff = [&](int kb, int kk) { return kb * 16 * D + kbase + (kx ^ (kk << 5)); };
+  const int vr = 4 * G + (i16 >> 2);
+  const int vbase = vr * D + (((i16 & 3) >> 1) << 3) + 4 * (i16 & 1);
+  const int vx = (vr & 7) << 4;
+  auto voff = [&](int db, int c, int h) { return (32 * c + 16 * h) * D + vbase + (vx ^ (db << 4)); };
 
-  // s[2 kb + j]: Sᵀ block of keys 32kb.., queries 32j.. (register r: key crow(kb, r, g), query n).
-  auto mask = [&](int k0, f32x16* s) {
+  // s[4kb + j]: Sᵀ block of keys 16kb.., queries 16j.. (register r: key 16kb + 4G + r, query 16j + i16).
+  auto mask = [&](int k0, f32x4* s) {
     if ((CAUSAL && k0 + kBC - 1 > qw + off) || (k0 + kBC > Nk)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < QB; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + crow(kb, r, g);
-            const bool dead = (key >= Nk) || (CAUSAL && key > qw + 32 * j + n + off);
-            s[2 * kb + j][r] = dead ? kNegInf : s[2 * kb + j][r];
+          for (int r = 0; r < 4; ++r) {
+            const int key = k0 + 16 * kb + 4 * G + r;
+            const bool dead = (key >= Nk) || (CAUSAL && key > qw + 16 * j + i16 + off);
+            s[4 * kb + j][r] = dead ? kNegInf : s[4 * kb + j][r];
           }
     }
   };
+  // Max over the four lanes that share a query (l, l ^ 16, l ^ 32, l ^ 48).
+  auto quad_max = [](float x) {
+    const float y = xhalf_max(x);
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  };
+  auto quad_sum = [](float x) {
+    const float y = xhalf_sum(x);
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  };
 
-  f32x16 oacc[DBLK][2];
+  f32x4 oacc[DB][QB];
 #pragma unroll
-  for (int b = 0; b < DBLK; ++b)
+  for (int b = 0; b < DB; ++b)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < QB; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[b][j][r] = 0.f;
-  float m_run[2] = {kNegInf, kNegInf};
-  float l_run[2] = {0.f, 0.f};
+      for (int r = 0; r < 4; ++r) oacc[b][j][r] = 0.f;
+  // m_run: reference max of s·scale·log2e of each query block, the same in the
+  // four lanes of a query; l_run: this lane's part of the row sum.
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    m_run[j] = kNegInf;
+    l_run[j] = 0.f;
+  }
 
   const int kv_end = CAUSAL ? max(min(Nk, q0 + kBR + off), 0) : Nk;
   const int ntiles = (kv_end + kBC - 1) / kBC;
@@ -675,140 +698,128 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
   if (ntiles > 0) issue_v(vbuf0, 0);
   wait_vm_all();
   __syncthreads();
-  f32x16 sa[4], sb[4];
+  f32x4 sa[KB * QB], sb[KB * QB];
   if (wnt > 0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbuf0 + kb * 32 * D + koff(kk));
+      for (int kk = 0; kk < KC; ++kk) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbuf0 + koff(kb, kk));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < QB; ++j) {
           if (kk == 0)
-            mfma_s0(sa[2 * kb + j], a, qreg[j][kk]);
+            mfma16_s0(sa[4 * kb + j], a, qreg[j][kk]);
           else
-            mfma_s(sa[2 * kb + j], a, qreg[j][kk]);
+            mfma16_s(sa[4 * kb + j], a, qreg[j][kk]);
         }
       }
     mfma_drain();
     mask(0, sa);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < QB; ++j) {
       float mx = kNegInf;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[2 * kb + j][r]);
-      m_run[j] = xhalf_max(mx) * scale_log2;
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sa[4 * kb + j][r]);
+      // a query with no visible key keeps a finite reference (its p are all 0)
+      const float m0 = quad_max(mx);
+      m_run[j] = m0 == kNegInf ? 0.f : m0 * scale_log2;
     }
   }
 
-  // One tile: NS slots of S(t+1) (one K read, two products each), then NP
-  // slots of Oᵀ += Vᵀ·Pᵀ (one Vᵀ read, two products each); P(t) pairs and
-  // the max of S(t+1) ride along as in the 32-query kernel.
-  constexpr int LOOK = kLook;
-  constexpr int NS = 2 * KSTEPS;
-  constexpr int NP = 4 * DBLK;
-  constexpr int NT = NS + NP;
-  // Softmax of S(t): value x's fma in half-slot fma_slot<PSPAN>(x) (the last
-  // pack lands two half-slots before the product that reads it).  Max of
-  // S(t+1): key block 0's values over half-slots MAXA .. MAXB-1, key block 1's
-  // over MAXB .. MAXN-1, each block at least five half-slots after its last
-  // product.
-  constexpr int PSPAN = 54;
-  constexpr int MAXA = 20, MAXB = 36, MAXN = 56;
-  constexpr int DEC = 2 * NT - 6;    // half-slots DEC, DEC + 1: its reduction and rescale test
-  // The loads of K(t+2) and V(t+1) go out one instruction every other
-  // half-slot from DMA0 on: issued in one burst, the four wavefronts' loads
-  // queue behind each other in the CU's memory pipeline and stall the issue.
-  constexpr int DMA0 = 1;
-  auto tile_slots = [&](bool maskn, int t, f32x16* sc, f32x16* sn, const bf16* kn, const bf16* vs,
-                        bf16* kdma, bf16* vdma) {
+  // One tile: 128 product slots.  Slots 0..63 compute Sᵀ(t+1), one K operand
+  // (block kb, k-step kk) per four slots, one query block per slot; slots
+  // 64..127 accumulate Oᵀ += Vᵀ·Pᵀ(t), one Vᵀ operand (key chunk c, block db)
+  // per four slots.  Every LDS operand is read three operands (twelve
+  // products) ahead of its first product.
+  constexpr int LOOK = 3;
+  constexpr int NSL = 128;
+  // Softmax of S(t): value x (0..63, pair x / 2) has its fma in slot
+  // fma_slot<PSPAN>(x), its exp one slot later; the pair's pack and sum one
+  // slot after its second exp, the row sum one after that.  Pairs go in the
+  // order their Pᵀ operands are used: key chunk c, query block j, key block
+  // 2c + h, register pair w (the last Pᵀ operand is packed by slot 92, five
+  // slots before its first product).  Max of S(t+1): two scores per v_max3,
+  // spread over slots MAX0 .. MAX0 + MAXN - 1 of the output half, where
+  // every block of S(t+1) is complete.
+  constexpr int PSPAN = 92;
+  constexpr int MAX0 = 66, MAXN = 56;
+  constexpr int DEC = MAX0 + MAXN;  // slots DEC .. DEC+3: the lazy-rescale test of each query block
+  // The eight tile loads of a wavefront (K(t+2), then V(t+1)) go out one every
+  // four slots from DMA0 on.
+  constexpr int DMA0 = 2;
+  auto tile_slots = [&](bool maskn, int t, f32x4* sc, f32x4* sn, const bf16* kn, const bf16* vs, bf16* kdma,
+                        bf16* vdma) {
     const uint32_t kt_base = t + 2 < ntiles ? tile_base(t + 2) : 0xF0000000u;
     const uint32_t vt_base = t + 1 < ntiles ? tile_base(t + 1) : 0xF0000000u;
     const auto rk2 = tile_rsrc(min(t + 2, ntiles - 1), 0);
     const auto rv1 = tile_rsrc(min(t + 1, ntiles - 1), 1);
-    auto kread = [&](int i) {
-      return *reinterpret_cast<const bf16x8*>(kn + (i / KSTEPS) * 32 * D + koff(i % KSTEPS));
-    };
-    auto vread = [&](int jj) {  // Vᵀ operand: key chunk jj / DBLK, d block jj % DBLK
-      const bf16* base = vs + voff(jj % DBLK) + 16 * (jj / DBLK) * D;
-      const bf16x4 lo = lds_read_tr4(base);
-      const bf16x4 hi = lds_read_tr4(base + 4 * D);
+    // operand n: K block n / 4, k-step n % 4 (n < 16); Vᵀ key chunk (n-16) / 8, block (n-16) % 8
+    auto oread = [&](int n) {
+      if (n < 16) return *reinterpret_cast<const bf16x8*>(kn + koff(n / 4, n % 4));
+      const int c = (n - 16) / DB, db = (n - 16) % DB;
+      const bf16x4 lo = lds_read_tr4(vs + voff(db, c, 0));
+      const bf16x4 hi = lds_read_tr4(vs + voff(db, c, 1));
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    float m_use[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) m_use[j] = (m_run[j] == kNegInf) ? 0.f : m_run[j];
     bf16x8 op[LOOK + 1];
-    u32x4 pw[2][4];  // P(t) of query block j, keys 16kk .. as packed bf16 pairs
+    u32x4 pw[QB][2];  // Pᵀ(t) of query block j, key chunk c, as packed bf16 pairs
     float px[32][2];  // score pair pi: s·scale·log2e − m, then its exp
     float pt[32];     // and the pair's sum
-    float nm[2];
+    float mx[QB];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) nm[j] = -m_use[j];
-    float mx[2] = {kNegInf, kNegInf};
-    float mt[2];
-    uint64_t need[2];
-    // max across the lane halves, scaled, and the lazy-rescale test
-    auto test = [&](int j) __attribute__((always_inline)) {
-      mt[j] = xhalf_max(mx[j]) * scale_log2;
-      need[j] = __builtin_amdgcn_ballot_w64(mt[j] > m_run[j] + kRescaleThreshold);
-    };
-    static_for<0, LOOK>([&](auto ic) __attribute__((always_inline)) { op[ic.value] = kread(ic.value); });
-    // Half-slots: one product each, so that with one wavefront per SIMD the
-    // VALU work issues between consecutive products instead of waiting behind
-    // a second one for the matrix pipe.
-    static_for<0, 2 * NT>([&](auto hc) __attribute__((always_inline)) {
-      constexpr int hs = decltype(hc)::value;
-      constexpr int sl = hs / 2, j = hs % 2;
-      constexpr int ahead = sl + LOOK;
-      if constexpr (j == 0) {
-        if constexpr (ahead < NS)
-          op[ahead % (LOOK + 1)] = kread(ahead);
-        else if constexpr (ahead < NT)
-          op[ahead % (LOOK + 1)] = vread(ahead - NS);
-      }
-      if constexpr (sl < NS) {
-        constexpr int kb = sl / KSTEPS, kk = sl % KSTEPS;
+    for (int j = 0; j < QB; ++j) mx[j] = kNegInf;
+    uint64_t need[QB];
+    static_for<0, LOOK>([&](auto ic) __attribute__((always_inline)) { op[ic.value] = oread(ic.value); });
+    static_for<0, NSL>([&](auto sc_) __attribute__((always_inline)) {
+      constexpr int s = decltype(sc_)::value;
+      constexpr int n = s / 4, j = s % 4;
+      if constexpr (j == 0 && n + LOOK < 32) op[(n + LOOK) % (LOOK + 1)] = oread(n + LOOK);
+      if constexpr (n < 16) {
+        constexpr int kb = n / 4, kk = n % 4;
         if constexpr (kk == 0)
-          mfma_s0_here(sn[2 * kb + j], op[sl % (LOOK + 1)], qreg[j][kk]);
+          mfma16_s0_here(sn[4 * kb + j], op[n % (LOOK + 1)], qreg[j][kk]);
         else
-          mfma_s_here(sn[2 * kb + j], op[sl % (LOOK + 1)], qreg[j][kk]);
+          mfma16_s_here(sn[4 * kb + j], op[n % (LOOK + 1)], qreg[j][kk]);
       } else {
-        constexpr int jj = sl - NS;
-        constexpr int kk = jj / DBLK, b = jj % DBLK;
-        mfma_o_here(oacc[b][j], op[sl % (LOOK + 1)], __builtin_bit_cast(bf16x8, pw[j][kk]));
+        constexpr int c = (n - 16) / DB, db = (n - 16) % DB;
+        mfma16_o_here(oacc[db][j], op[n % (LOOK + 1)], __builtin_bit_cast(bf16x8, pw[j][c]));
       }
-      // score pairs: pi = 8 kk + 4 jp + w  (kk = key chunk, jp = query block, w = pair inside it)
+      // score pairs: pi = 16c + 4jp + 2h + w (key chunk c, query block jp, key block 2c + h, registers 2w, 2w+1)
       static_for<0, 32>([&](auto pic) __attribute__((always_inline)) {
         constexpr int pi = decltype(pic)::value;
-        constexpr int kk = pi / 8, jp = (pi / 4) % 2, w = pi % 4;
-        constexpr int kb = kk / 2, r = 8 * (kk % 2) + 2 * w;
+        constexpr int c = pi / 16, jp = (pi / 4) % 4, h = (pi / 2) % 2, w = pi % 2;
+        constexpr int blk = 4 * (2 * c + h) + jp, r = 2 * w;
         constexpr int f0 = fma_slot<PSPAN>(2 * pi), f1 = fma_slot<PSPAN>(2 * pi + 1), pk = f1 + 2;
-        static_assert(pk <= 2 * NS + 8 * kk + jp - 2, "a P chunk must be packed two half-slots before its product");
-        if constexpr (f0 == hs) fma_here(px[pi][0], sc[2 * kb + jp][r], scale_log2, nm[jp]);
-        if constexpr (f1 == hs) fma_here(px[pi][1], sc[2 * kb + jp][r + 1], scale_log2, nm[jp]);
-        if constexpr (f0 + 1 == hs) exp2_here(px[pi][0], px[pi][0]);
-        if constexpr (f1 + 1 == hs) exp2_here(px[pi][1], px[pi][1]);
-        if constexpr (pk == hs) {
+        static_assert(pk <= 64 + 32 * c + jp - 2, "a Pᵀ operand must be packed two slots before its product");
+        if constexpr (f0 == s) fms_here(px[pi][0], sc[blk][r], scale_log2, m_run[jp]);
+        if constexpr (f1 == s) fms_here(px[pi][1], sc[blk][r + 1], scale_log2, m_run[jp]);
+        if constexpr (f0 + 1 == s) exp2_here(px[pi][0], px[pi][0]);
+        if constexpr (f1 + 1 == s) exp2_here(px[pi][1], px[pi][1]);
+        if constexpr (pk == s) {
           uint32_t packed;
           pack_here(packed, px[pi][0], px[pi][1]);
-          pw[jp][kk][w] = packed;
+          pw[jp][c][2 * h + w] = packed;
           add_here(pt[pi], px[pi][0], px[pi][1]);
         }
-        if constexpr (pk + 1 == hs) accumulate_here(l_run[jp], pt[pi]);  // fp32 sum of the unrounded p
+        if constexpr (pk + 1 == s) accumulate_here(l_run[jp], pt[pi]);  // fp32 sum of the unrounded p
       });
+      // max of S(t+1): value pair v of block (kb, jq) = (v / 8, (v / 2) % 4), registers 2(v % 2)..
       static_for<0, 32>([&](auto vc_) __attribute__((always_inline)) {
-        constexpr int v = 2 * decltype(vc_)::value;  // values v, v+1 of S(t+1)
-        constexpr int blk = v / 16;                  // block 2kb + j
-        constexpr int at = v < 32 ? MAXA + (v * (MAXB - MAXA)) / 32 : MAXB + ((v - 32) * (MAXN - MAXB)) / 32;
+        constexpr int v = decltype(vc_)::value;
+        constexpr int kb = v / 8, jq = (v / 2) % 4, r = 2 * (v % 2);
+        constexpr int at = MAX0 + (v * MAXN) / 32;
+        static_assert(at >= 16 * kb + 12 + jq + 4, "a max reads its block four products after the block's last");
         static_assert(at < DEC, "the max of S(t+1) precedes its test");
-        if constexpr (at == hs) max3_here(mx[blk % 2], sn[blk][v % 16], sn[blk][v % 16 + 1]);
+        if constexpr (at == s) max3_here(mx[jq], sn[4 * kb + jq][r], sn[4 * kb + jq][r + 1]);
       });
-      if constexpr (hs == DEC || hs == DEC + 1) test(hs - DEC);
-      if constexpr (hs >= DMA0 && (hs - DMA0) % 2 == 0 && (hs - DMA0) / 2 < 2 * DMA_PER_WAVE) {
-        constexpr int i = (hs - DMA0) / 2;
+      // lazy-rescale test of query block s - DEC: any lane whose part of the
+      // row max exceeds the reference by the threshold
+      if constexpr (s >= DEC && s < DEC + QB)
+        need[s - DEC] = __builtin_amdgcn_ballot_w64(mx[s - DEC] * scale_log2 > m_run[s - DEC] + kRescaleThreshold);
+      if constexpr (s >= DMA0 && (s - DMA0) % 4 == 0 && (s - DMA0) / 4 < 2 * DMA_PER_WAVE) {
+        constexpr int i = (s - DMA0) / 4;
         if constexpr (i < DMA_PER_WAVE)
           issue_k1(kdma, rk2, kt_base, i);
         else
@@ -821,38 +832,46 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
       if (maskn) {
         mask((t + 1) * kBC, sn);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < QB; ++j) {
           mx[j] = kNegInf;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx[j] = fmaxf(mx[j], sn[2 * kb + j][r]);
-          test(j);
+            for (int r = 0; r < 4; ++r) mx[j] = fmaxf(mx[j], sn[4 * kb + j][r]);
+          need[j] = __builtin_amdgcn_ballot_w64(mx[j] * scale_log2 > m_run[j] + kRescaleThreshold);
         }
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < QB; ++j) {
         if (need[j]) {
           mfma_drain();
-          const float m_new = fmaxf(m_run[j], mt[j]);
+          const float mt = quad_max(mx[j]) * scale_log2;
+          const float m_new = fmaxf(m_run[j], mt);
           const float alpha = exp2_fast(m_run[j] - m_new);
           l_run[j] *= alpha;
-          // in place in the accumulation registers, one element at a time
+          // Each accumulator block goes out of the accumulation registers and
+          // back through this lane's own 16 bytes of LDS, so the compiler
+          // never holds the output blocks anywhere but in those registers.
 #pragma unroll
-          for (int b = 0; b < DBLK; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              float x = oacc[b][j][r];
-              acc_scale(x, alpha);
-              oacc[b][j][r] = x;
-            }
+          for (int b = 0; b < DB; ++b) {
+            f32x4 x;
+            asm volatile("ds_write_b128 %1, %2\n\ts_waitcnt lgkmcnt(0)\n\tds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                         : "=&v"(x)
+                         : "v"(rsc_lane), "a"(oacc[b][j])
+                         : "memory");
+            x = x * alpha;
+            asm volatile("ds_write_b128 %1, %2\n\ts_waitcnt lgkmcnt(0)\n\tds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                         : "=&a"(oacc[b][j])
+                         : "v"(rsc_lane), "v"(x)
+                         : "memory");
+          }
           m_run[j] = m_new;
         }
       }
     }
   };
 
-  auto step = [&](int t, f32x16* sc, f32x16* sn, bf16* kc, bf16* kn, bf16* vc, bf16* vn) {
+  auto step = [&](int t, f32x4* sc, f32x4* sn, bf16* kc, bf16* kn, bf16* vc, bf16* vn) {
     const int k0 = t * kBC;
     wait_vm_all();
     __syncthreads();  // K(t+1) and V(t) resident for every wave; tile t-1 fully consumed
@@ -873,29 +892,27 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
     tile_slots((CAUSAL && k0n + kBC - 1 > qw + off) || (k0n + kBC > Nk), t, sc, sn, kn, vc, kc, vn);
   };
 
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = 0; t < ntiles; t += 2) {  // unrolled by two so S(t) and S(t+1) swap registers
     step(t, sa, sb, kbuf0, kbuf1, vbuf0, vbuf1);
     if (t + 1 < ntiles) step(t + 1, sb, sa, kbuf1, kbuf0, vbuf1, vbuf0);
   }
   mfma_drain();
 
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int qrow = qw + 32 * j + n;
+  for (int j = 0; j < QB; ++j) {
+    const float l_tot = quad_sum(l_run[j]);
+    const int qrow = qw + 16 * j + i16;
     if (qrow >= N) continue;
-    const float l_tot = xhalf_sum(l_run[j]);
     const float inv = hv.cut ? kNaN : (l_tot > 0.f ? 1.f / l_tot : 0.f);
     bf16* Orow = O + hv.q_off + (size_t)qrow * hv.qs;
 #pragma unroll
-    for (int b = 0; b < DBLK; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[b][j][4 * i + 0] * inv, oacc[b][j][4 * i + 1] * inv);
-        w[1] = pack_bf16x2(oacc[b][j][4 * i + 2] * inv, oacc[b][j][4 * i + 3] * inv);
-        *reinterpret_cast<u32x2*>(Orow + 32 * b + 8 * i + 4 * g) = w;
-      }
-    if (LSE != nullptr && g == 0)
+    for (int b = 0; b < DB; ++b) {
+      u32x2 w;
+      w[0] = pack_bf16x2(oacc[b][j][0] * inv, oacc[b][j][1] * inv);
+      w[1] = pack_bf16x2(oacc[b][j][2] * inv, oacc[b][j][3] * inv);
+      *reinterpret_cast<u32x2*>(Orow + 16 * b + 4 * G) = w;
+    }
+    if (LSE != nullptr && G == 0)
       LSE[hv.st_off + qrow] = hv.cut ? kNaN : (l_tot > 0.f ? (m_run[j] + log2_fast(l_tot)) * kLn2 : kNegInf);
   }
 }
