@@ -402,7 +402,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm-s", type=float, default=None, metavar="SECONDS",
                     help="with --only: untimed seconds of back-to-back calls after the warm-up steps "
-                         f"(default {SECONDARY_WARM_S}: a working card, as the full run times every record)")
+                         f"(default: 0 for fwd, as the headline record; {SECONDARY_WARM_S} for the others, as their records)")
     ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
                     help="with --only: afterwards launch the path back to back for SECONDS while amd-smi "
                          "samples board power and clocks (decode: without the cache flush)")
@@ -419,7 +419,7 @@ def main():
 
     if args.only:
         _POWER["seconds"] = args.power
-        ws = args.warm_s if args.warm_s is not None else SECONDARY_WARM_S
+        ws = args.warm_s if args.warm_s is not None else (0.0 if args.only == "fwd" else SECONDARY_WARM_S)
         rec = {"fwd": lambda: bench_forward("c2a", args.steps, args.warmup, warm_s=ws),
                "fwd32k": lambda: bench_forward("c2b", args.steps, args.warmup, warm_s=ws),
                "fwdnc": lambda: bench_forward("c2c", args.steps, args.warmup, warm_s=ws),
