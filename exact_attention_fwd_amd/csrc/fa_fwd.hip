@@ -645,7 +645,7 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
   const int vx = (vr & 7) << 4;
   auto voff = [&](int db, int c, int h) { return (32 * c + 16 * h) * D + vbase + (vx ^ (db << 4)); };
 
-  // s[QB·kb + j]: Sᵀ block of keys 16kb.., queries 16j.. (register r: key 16kb + 4G + r, query 16j + i16).
+  // s[4kb + j]: Sᵀ block of keys 16kb.., queries 16j.. (register r: key 16kb + 4G + r, query 16j + i16).
   auto mask = [&](int k0, f32x4* s) {
     if ((CAUSAL && k0 + kBC - 1 > qw + off) || (k0 + kBC > Nk)) {
 #pragma unroll
@@ -656,7 +656,7 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
           for (int r = 0; r < 4; ++r) {
             const int key = k0 + 16 * kb + 4 * G + r;
             const bool dead = (key >= Nk) || (CAUSAL && key > qw + 16 * j + i16 + off);
-            s[QB * kb + j][r] = dead ? kNegInf : s[QB * kb + j][r];
+            s[4 * kb + j][r] = dead ? kNegInf : s[4 * kb + j][r];
           }
     }
   };
@@ -708,9 +708,9 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
 #pragma unroll
         for (int j = 0; j < QB; ++j) {
           if (kk == 0)
-            mfma16_s0(sa[QB * kb + j], a, qreg[j][kk]);
+            mfma16_s0(sa[4 * kb + j], a, qreg[j][kk]);
           else
-            mfma16_s(sa[QB * kb + j], a, qreg[j][kk]);
+            mfma16_s(sa[4 * kb + j], a, qreg[j][kk]);
         }
       }
     mfma_drain();
@@ -721,7 +721,7 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sa[QB * kb + j][r]);
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sa[4 * kb + j][r]);
       // a query with no visible key keeps a finite reference (its p are all 0)
       const float m0 = quad_max(mx);
       m_run[j] = m0 == kNegInf ? 0.f : m0 * scale_log2;
@@ -779,9 +779,9 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
       if constexpr (n < 16) {
         constexpr int kb = n / 4, kk = n % 4;
         if constexpr (kk == 0)
-          mfma16_s0_here(sn[QB * kb + j], op[n % (LOOK + 1)], qreg[j][kk]);
+          mfma16_s0_here(sn[4 * kb + j], op[n % (LOOK + 1)], qreg[j][kk]);
         else
-          mfma16_s_here(sn[QB * kb + j], op[n % (LOOK + 1)], qreg[j][kk]);
+          mfma16_s_here(sn[4 * kb + j], op[n % (LOOK + 1)], qreg[j][kk]);
       } else {
         constexpr int c = (n - 16) / DB, db = (n - 16) % DB;
         mfma16_o_here(oacc[db][j], op[n % (LOOK + 1)], __builtin_bit_cast(bf16x8, pw[j][c]));
@@ -790,7 +790,7 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
       static_for<0, 32>([&](auto pic) __attribute__((always_inline)) {
         constexpr int pi = decltype(pic)::value;
         constexpr int c = pi / 16, jp = (pi / 4) % 4, h = (pi / 2) % 2, w = pi % 2;
-        constexpr int blk = QB * (2 * c + h) + jp, r = 2 * w;
+        constexpr int blk = 4 * (2 * c + h) + jp, r = 2 * w;
         constexpr int f0 = fma_slot<PSPAN>(2 * pi), f1 = fma_slot<PSPAN>(2 * pi + 1), pk = f1 + 2;
         static_assert(pk <= 64 + 32 * c + jp - 2, "a Pᵀ operand must be packed two slots before its product");
         if constexpr (f0 == s) fms_here(px[pi][0], sc[blk][r], scale_log2, m_run[jp]);
@@ -812,7 +812,7 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
         constexpr int at = MAX0 + (v * MAXN) / 32;
         static_assert(at >= 16 * kb + 12 + jq + 4, "a max reads its block four products after the block's last");
         static_assert(at < DEC, "the max of S(t+1) precedes its test");
-        if constexpr (at == s) max3_here(mx[jq], sn[QB * kb + jq][r], sn[QB * kb + jq][r + 1]);
+        if constexpr (at == s) max3_here(mx[jq], sn[4 * kb + jq][r], sn[4 * kb + jq][r + 1]);
       });
       // lazy-rescale test of query block s - DEC: any lane whose part of the
       // row max exceeds the reference by the threshold
@@ -837,7 +837,7 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) mx[j] = fmaxf(mx[j], sn[QB * kb + j][r]);
+            for (int r = 0; r < 4; ++r) mx[j] = fmaxf(mx[j], sn[4 * kb + j][r]);
           need[j] = __builtin_amdgcn_ballot_w64(mx[j] * scale_log2 > m_run[j] + kRescaleThreshold);
         }
       }
