@@ -305,18 +305,9 @@ __device__ __forceinline__ void mfma_s(f32x16& s, const bf16x8& a, const bf16x8&
 __device__ __forceinline__ void mfma_o(f32x16& o, const bf16x8& a, const bf16x8& p) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(p));
 }
-// The same products pinned in program order (volatile), for software
-// pipelines whose slots are laid out by hand.
-__device__ __forceinline__ void mfma_s0_here(f32x16& s, const bf16x8& a, const bf16x8& q) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "a"(q));
-}
-__device__ __forceinline__ void mfma_s_here(f32x16& s, const bf16x8& a, const bf16x8& q) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "a"(q));
-}
-__device__ __forceinline__ void mfma_o_here(f32x16& o, const bf16x8& a, const bf16x8& p) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(p));
-}
-// The same on 16x16x32 products (result: 4 registers per lane).
+// The same on 16x16x32 products (result: 4 registers per lane); the _here
+// forms are volatile, pinned in program order for software pipelines whose
+// slots are laid out by hand.
 __device__ __forceinline__ void mfma16_s0(f32x4& s, const bf16x8& a, const bf16x8& q) {
   asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "a"(q));
 }
@@ -333,14 +324,10 @@ __device__ __forceinline__ void mfma16_o_here(f32x4& o, const bf16x8& a, const b
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(p));
 }
 // Softmax operations for software pipelines laid out by hand (the w64
-// forward), each one instruction that stays where it is
-// written (between the products of its pipeline slot).  The callers place
-// every consumer of a result at least one slot (one 32-cycle product) after
-// its producer, so no result is read by the next instruction and no wait
-// states are needed.
-__device__ __forceinline__ void fma_here(float& d, float a, float b, float c) {
-  asm volatile("v_fma_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
-}
+// forward), each one instruction that stays where it is written (between
+// the products of its pipeline slot).  The callers place every consumer of
+// a result at least one slot (one product) after its producer, so no result
+// is read by the next instruction and no wait states are needed.
 // d = a·b − c (c negated by the instruction's source modifier).
 __device__ __forceinline__ void fms_here(float& d, float a, float b, float c) {
   asm volatile("v_fma_f32 %0, %1, %2, -%3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
@@ -355,14 +342,7 @@ __device__ __forceinline__ void pack_here(uint32_t& d, float lo, float hi) {
   asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(d) : "v"(lo), "v"(hi));
 }
 
-// x *= alpha for a value held in an accumulation register.
-__device__ __forceinline__ void acc_scale(float& x, float alpha) {
-  float t;
-  asm("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-      : "+a"(x), "=&v"(t)
-      : "v"(alpha));
-}
-// More wait states than a 32x32x16 product needs before its result is read.
+// More wait states than a 32x32x16 or 16x16x32 product needs before its result is read.
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 }  // namespace fa
