@@ -566,3 +566,54 @@ def test_rope_operands_are_the_exact_rotation_rounded():
         ro, rl = oracle.attention_forward_rope(q, k, v, c, s, causal=True, interleaved=interleaved)
         check(f"rope exact rounding LSE interleaved={interleaved}", to64(lse), rl, 1e-4)
         assert torch.equal(o.cpu(), v)  # one key: O is its V row
+
+
+# ------------------------------------------------------- seeded random sweeps
+def _random_dense_cases(count=16, seed=2026):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        hkv = int(rng.choice([1, 2, 4]))
+        cases.append((int(rng.integers(1, 3)), hkv * int(rng.choice([1, 2, 4])), hkv, int(rng.integers(1, 900)),
+                      int(rng.choice([64, 128])), bool(rng.integers(0, 2)), 300 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_dense_cases(), ids=lambda c: "B%d_H%d_kv%d_N%d_d%d_%s" % (
+    c[0], c[1], c[2], c[3], c[4], "causal" if c[5] else "full"))
+def test_forward_random_shapes(case):
+    """Seeded random shapes through the forward (batch 1-2, 1-16 query heads on
+    1-4 key/value heads, 1-899 queries, d = 64 or 128, causal or not), every
+    output element against the fp64 oracle: lengths that are not multiples of
+    the 16-, 32- and 64-row blocks of either forward kernel."""
+    B, H, Hkv, N, d, causal, seed = case
+    print(f"[random fwd] B={B} H={H} Hkv={Hkv} N={N} d={d} causal={causal}", flush=True)
+    q, k, v = workloads.gqa_inputs(B, H, Hkv, N, d, "bf16", seed=seed)
+    o, lse = fa().forward(*cuda(q, k, v), causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_forward_gqa(q, k, v, causal=causal, scale=1 / math.sqrt(d))
+    check("random O", to64(o), ro, BF16_MAX, BF16_MEAN)
+    check("random LSE", to64(lse), rl, LSE_MAX)
+
+
+def _random_varlen_cases(count=6, seed=2027):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        n = int(rng.integers(1, 6))
+        lens = [int(x) for x in rng.integers(0, 700, n)]
+        lens[int(rng.integers(0, n))] = max(lens[0], 1)  # at least one non-empty sequence
+        hkv = int(rng.choice([1, 2, 4]))
+        cases.append((lens, hkv * int(rng.choice([1, 2])), hkv, int(rng.choice([64, 128])), bool(rng.integers(0, 2)),
+                      400 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_varlen_cases(), ids=lambda c: "n%d_H%d_kv%d_d%d_%s" % (
+    len(c[0]), c[1], c[2], c[3], "causal" if c[4] else "full"))
+def test_varlen_random_batches(case):
+    """Seeded random packed batches (1-5 sequences of 0-699 tokens, grouped or
+    not, d = 64 or 128, causal or not): forward and backward, every element
+    against the oracle."""
+    lens, H, Hkv, d, causal, seed = case
+    _varlen_compare(lens, H, Hkv, d, causal, seed=seed)
