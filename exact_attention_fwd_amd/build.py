@@ -13,6 +13,12 @@ bytes into accumulation registers whose fourth register was never written
 (its copy was kept in another register that the reload on that path did
 not read back), which produced NaN gradients.  Keeping every kernel free of
 spills keeps that code path out of the compiler entirely.
+
+It also fails if the device assembly of any kernel places an inline-asm
+matrix instruction closer to a dependent instruction than the wait states
+gfx950 requires (asm_lint): the compiler pads only the instructions it emits
+itself.  Each source is compiled a second time with -S for that check, with
+the same flags, in parallel with the object build.
 """
 from __future__ import annotations
 
@@ -64,18 +70,23 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         raise RuntimeError(f"no HIP sources under {CSRC}")
     tmp = tempfile.mkdtemp(prefix="fa_build_")
     try:
-        objs, procs = [], []
+        objs, asms, procs = [], [], []
+        asm_flags = [f for f in HIPCC_FLAGS if not f.startswith("-Rpass")]
         for src in srcs:
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
-            cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-c", src, "-o", obj]
-            if verbose:
-                print(" ".join(cmd), flush=True)
-            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+            asm = os.path.join(tmp, os.path.basename(src) + ".s")
+            for cmd, check in (([cc, *HIPCC_FLAGS, "-I", INCLUDE, "-c", src, "-o", obj], True),
+                               ([cc, *asm_flags, "-I", INCLUDE, "--cuda-device-only", "-S", src, "-o", asm], False)):
+                if verbose:
+                    print(" ".join(cmd), flush=True)
+                procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT), check))
+                if len(procs) >= jobs:
+                    _wait(procs.pop(0), verbose)
             objs.append(obj)
-            if len(procs) >= jobs:
-                _wait(procs.pop(0), verbose)
+            asms.append(asm)
         for p in procs:
             _wait(p, verbose)
+        _lint(asms, verbose)
         out_tmp = LIB_PATH + ".tmp"
         link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp,
                 "-Wl,-rpath,/opt/rocm/lib"]
@@ -116,8 +127,22 @@ def _check_resources(src, text):
     return res
 
 
+def _lint(asms, verbose):
+    from . import asm_lint
+    found = []
+    for path in asms:
+        with open(path) as f:
+            found.extend(asm_lint.check(f.read()))
+    if found:
+        shown = "\n".join(str(x) for x in found[:20])
+        raise RuntimeError(f"inline-asm matrix instructions closer than gfx950's wait states "
+                           f"({len(found)} pairs, refused):\n{shown}")
+    if verbose:
+        print(f"asm lint: {len(asms)} sources, no inline-asm wait-state violations", flush=True)
+
+
 def _wait(item, verbose):
-    src, p = item
+    src, p, check = item
     out, _ = p.communicate()
     text = out.decode(errors="replace")
     # hipcc's host pass does not know the packed-fp32 feature name; that note is harmless
@@ -126,6 +151,8 @@ def _wait(item, verbose):
              if "packed-fp32-ops" not in ln and "remark:" not in ln and not re.match(r"\s*(\d+\s*)?\|", ln)]
     if p.returncode != 0:
         raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n" + "\n".join(lines))
+    if not check:
+        return
     res = _check_resources(src, text)
     if verbose:
         if lines:
