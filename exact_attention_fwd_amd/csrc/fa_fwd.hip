@@ -58,6 +58,12 @@ constexpr int fma_slot(int x) {
 // output, its normaliser and the logsumexp all use the same reference m, so
 // the result is the same exact quantity (only rounding differs).
 constexpr float kRescaleThreshold = 8.0f;
+// The d = 128 forward's sum check: a row whose sum passes 2^20 is scaled back
+// by a power of two; one whose sum reaches 2^40 (or is not a number) sends its
+// workgroup through the exact-max loop instead.  A sum below 2^40 bounds every
+// p, and each partial output by 2^40 times the largest |v|.
+constexpr float kSumRescale = 1048576.0f;     // 2^20
+constexpr float kSumLimit = 1099511627776.0f;  // 2^40
 
 constexpr int kPage = 256;  // tokens per page of a paged key/value pool
 // Slots between an LDS operand read and the product that consumes it.
@@ -673,60 +679,34 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
   };
 
   f32x4 oacc[DB][QB];
-#pragma unroll
-  for (int b = 0; b < DB; ++b)
-#pragma unroll
-    for (int j = 0; j < QB; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) oacc[b][j][r] = 0.f;
-  // m_run: reference max of s·scale·log2e of each query block, the same in the
+  // m_run: reference of s·scale·log2e of each query block, the same in the
   // four lanes of a query; l_run: this lane's part of the row sum.
   float m_run[QB], l_run[QB];
-#pragma unroll
-  for (int j = 0; j < QB; ++j) {
-    m_run[j] = kNegInf;
-    l_run[j] = 0.f;
-  }
 
   const int kv_end = CAUSAL ? max(min(Nk, q0 + kBR + off), 0) : Nk;
   const int ntiles = (kv_end + kBC - 1) / kBC;
   const int wlast = min(qw + 63, N - 1) + off;  // the wave's last visible key (causal)
   const int wnt = (qw >= N) ? 0 : (CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / kBC + 1)) : ntiles);
 
-  if (ntiles > 0) issue_k(kbuf0, 0);
-  if (ntiles > 1) issue_k(kbuf1, 1);
-  if (ntiles > 0) issue_v(vbuf0, 0);
-  wait_vm_all();
-  __syncthreads();
-  f32x4 sa[KB * QB], sb[KB * QB];
-  if (wnt > 0) {
+  // Output block j of this lane's query times alpha.  Each accumulator block
+  // goes out of the accumulation registers and back through this lane's own
+  // 16 bytes of LDS, so the compiler never holds the output blocks anywhere
+  // but in those registers.
+  auto scale_out = [&](int j, float alpha) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int kk = 0; kk < KC; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbuf0 + koff(kb, kk));
-#pragma unroll
-        for (int j = 0; j < QB; ++j) {
-          if (kk == 0)
-            mfma16_s0(sa[4 * kb + j], a, qreg[j][kk]);
-          else
-            mfma16_s(sa[4 * kb + j], a, qreg[j][kk]);
-        }
-      }
-    mfma_drain();
-    mask(0, sa);
-#pragma unroll
-    for (int j = 0; j < QB; ++j) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sa[4 * kb + j][r]);
-      // a query with no visible key keeps a finite reference (its p are all 0)
-      const float m0 = quad_max(mx);
-      m_run[j] = m0 == kNegInf ? 0.f : m0 * scale_log2;
+    for (int b = 0; b < DB; ++b) {
+      f32x4 x;
+      asm volatile("ds_write_b128 %1, %2\n\ts_waitcnt lgkmcnt(0)\n\tds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                   : "=&v"(x)
+                   : "v"(rsc_lane), "a"(oacc[b][j])
+                   : "memory");
+      x = x * alpha;
+      asm volatile("ds_write_b128 %1, %2\n\ts_waitcnt lgkmcnt(0)\n\tds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                   : "=&a"(oacc[b][j])
+                   : "v"(rsc_lane), "v"(x)
+                   : "memory");
     }
-  }
+  };
 
   // One tile: 128 product slots.  Slots 0..63 compute Sᵀ(t+1), one K operand
   // (block kb, k-step kk) per four slots, one query block per slot; slots
@@ -740,17 +720,29 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
   // slot after its second exp, the row sum one after that.  Pairs go in the
   // order their Pᵀ operands are used: key chunk c, query block j, key block
   // 2c + h, register pair w (the last Pᵀ operand is packed by slot 92, five
-  // slots before its first product).  Max of S(t+1): two scores per v_max3,
-  // spread over slots MAX0 .. MAX0 + MAXN - 1 of the output half, where
-  // every block of S(t+1) is complete.
+  // slots before its first product).
+  // Two ways to keep p bounded (EXACT below):
+  //  * EXACT: the max of S(t+1), two scores per v_max3, spread over slots
+  //    MAX0 .. MAX0 + MAXN - 1 of the output half, where every block of
+  //    S(t+1) is complete; the reference moves (rescaling output and
+  //    normaliser) when that max exceeds it by kRescaleThreshold.
+  //  * sum check: no max at all.  The reference is the first tile's row max;
+  //    after each tile a row whose sum exceeds kSumRescale has output and sum
+  //    scaled by an exact power of two 2^-e and e added to its reference.  p
+  //    never exceeds the row sum, so a sum below kSumLimit bounds every p and
+  //    every partial output; a tile that lifts a sum past it (a jump of the
+  //    scores by more than ~20 powers of two within one tile) or makes it
+  //    non-finite marks the workgroup, which then recomputes its rows with
+  //    EXACT.
   constexpr int PSPAN = 92;
   constexpr int MAX0 = 66, MAXN = 56;
-  constexpr int DEC = MAX0 + MAXN;  // slots DEC .. DEC+3: the lazy-rescale test of each query block
+  constexpr int DEC = MAX0 + MAXN;  // slots DEC .. DEC+3: the rescale test of each query block
   // The eight tile loads of a wavefront (K(t+2), then V(t+1)) go out one every
   // four slots from DMA0 on.
   constexpr int DMA0 = 2;
-  auto tile_slots = [&](bool maskn, int t, f32x4* sc, f32x4* sn, const bf16* kn, const bf16* vs, bf16* kdma,
-                        bf16* vdma) {
+  auto tile_slots = [&](auto exact_c, bool maskn, int t, f32x4* sc, f32x4* sn, const bf16* kn, const bf16* vs,
+                        bf16* kdma, bf16* vdma, bool& bad) {
+    constexpr bool EXACT = decltype(exact_c)::value;
     const uint32_t kt_base = t + 2 < ntiles ? tile_base(t + 2) : 0xF0000000u;
     const uint32_t vt_base = t + 1 < ntiles ? tile_base(t + 1) : 0xF0000000u;
     const auto rk2 = tile_rsrc(min(t + 2, ntiles - 1), 0);
@@ -793,6 +785,7 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
         constexpr int blk = 4 * (2 * c + h) + jp, r = 2 * w;
         constexpr int f0 = fma_slot<PSPAN>(2 * pi), f1 = fma_slot<PSPAN>(2 * pi + 1), pk = f1 + 2;
         static_assert(pk <= 64 + 32 * c + jp - 2, "a Pᵀ operand must be packed two slots before its product");
+        static_assert(pk + 1 < DEC, "the row sums are complete before their test");
         if constexpr (f0 == s) fms_here(px[pi][0], sc[blk][r], scale_log2, m_run[jp]);
         if constexpr (f1 == s) fms_here(px[pi][1], sc[blk][r + 1], scale_log2, m_run[jp]);
         if constexpr (f0 + 1 == s) exp2_here(px[pi][0], px[pi][0]);
@@ -805,19 +798,26 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
         }
         if constexpr (pk + 1 == s) accumulate_here(l_run[jp], pt[pi]);  // fp32 sum of the unrounded p
       });
-      // max of S(t+1): value pair v of block (kb, jq) = (v / 8, (v / 2) % 4), registers 2(v % 2)..
-      static_for<0, 32>([&](auto vc_) __attribute__((always_inline)) {
-        constexpr int v = decltype(vc_)::value;
-        constexpr int kb = v / 8, jq = (v / 2) % 4, r = 2 * (v % 2);
-        constexpr int at = MAX0 + (v * MAXN) / 32;
-        static_assert(at >= 16 * kb + 12 + jq + 4, "a max reads its block four products after the block's last");
-        static_assert(at < DEC, "the max of S(t+1) precedes its test");
-        if constexpr (at == s) max3_here(mx[jq], sn[4 * kb + jq][r], sn[4 * kb + jq][r + 1]);
-      });
-      // lazy-rescale test of query block s - DEC: any lane whose part of the
-      // row max exceeds the reference by the threshold
-      if constexpr (s >= DEC && s < DEC + QB)
-        need[s - DEC] = __builtin_amdgcn_ballot_w64(mx[s - DEC] * scale_log2 > m_run[s - DEC] + kRescaleThreshold);
+      if constexpr (EXACT) {
+        // max of S(t+1): value pair v of block (kb, jq) = (v / 8, (v / 2) % 4), registers 2(v % 2)..
+        static_for<0, 32>([&](auto vc_) __attribute__((always_inline)) {
+          constexpr int v = decltype(vc_)::value;
+          constexpr int kb = v / 8, jq = (v / 2) % 4, r = 2 * (v % 2);
+          constexpr int at = MAX0 + (v * MAXN) / 32;
+          static_assert(at >= 16 * kb + 12 + jq + 4, "a max reads its block four products after the block's last");
+          static_assert(at < DEC, "the max of S(t+1) precedes its test");
+          if constexpr (at == s) max3_here(mx[jq], sn[4 * kb + jq][r], sn[4 * kb + jq][r + 1]);
+        });
+        // lazy-rescale test of query block s - DEC: any lane whose part of the
+        // row max exceeds the reference by the threshold
+        if constexpr (s >= DEC && s < DEC + QB)
+          need[s - DEC] = __builtin_amdgcn_ballot_w64(mx[s - DEC] * scale_log2 > m_run[s - DEC] + kRescaleThreshold);
+      } else {
+        // sum test of query block s - DEC: any lane whose part of the row sum
+        // exceeds kSumRescale or is not a number
+        if constexpr (s >= DEC && s < DEC + QB)
+          need[s - DEC] = __builtin_amdgcn_ballot_w64(!(l_run[s - DEC] <= kSumRescale));
+      }
       if constexpr (s >= DMA0 && (s - DMA0) % 4 == 0 && (s - DMA0) / 4 < 2 * DMA_PER_WAVE) {
         constexpr int i = (s - DMA0) / 4;
         if constexpr (i < DMA_PER_WAVE)
@@ -828,75 +828,136 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
       __builtin_amdgcn_sched_barrier(0);
     });
 
-    if (t + 1 < wnt) {
-      if (maskn) {
-        mask((t + 1) * kBC, sn);
+    if constexpr (EXACT) {
+      if (t + 1 < wnt) {
+        if (maskn) {
+          mask((t + 1) * kBC, sn);
+#pragma unroll
+          for (int j = 0; j < QB; ++j) {
+            mx[j] = kNegInf;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) mx[j] = fmaxf(mx[j], sn[4 * kb + j][r]);
+            need[j] = __builtin_amdgcn_ballot_w64(mx[j] * scale_log2 > m_run[j] + kRescaleThreshold);
+          }
+        }
 #pragma unroll
         for (int j = 0; j < QB; ++j) {
-          mx[j] = kNegInf;
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) mx[j] = fmaxf(mx[j], sn[4 * kb + j][r]);
-          need[j] = __builtin_amdgcn_ballot_w64(mx[j] * scale_log2 > m_run[j] + kRescaleThreshold);
+          if (need[j]) {
+            mfma_drain();
+            const float mt = quad_max(mx[j]) * scale_log2;
+            const float m_new = fmaxf(m_run[j], mt);
+            const float alpha = exp2_fast(m_run[j] - m_new);
+            l_run[j] *= alpha;
+            scale_out(j, alpha);
+            m_run[j] = m_new;
+          }
         }
       }
+    } else {
+      if (t + 1 < wnt && maskn) mask((t + 1) * kBC, sn);
+      // Every tile, the last one included (a sum past kSumLimit there still
+      // means a partial output may have overflowed).
 #pragma unroll
       for (int j = 0; j < QB; ++j) {
         if (need[j]) {
           mfma_drain();
-          const float mt = quad_max(mx[j]) * scale_log2;
-          const float m_new = fmaxf(m_run[j], mt);
-          const float alpha = exp2_fast(m_run[j] - m_new);
+          const float lq = quad_sum(l_run[j]);  // the row sum of this lane's query
+          const bool over = !(lq < kSumLimit);
+          bad = bad || over;
+          // lq = f·2^e with f in [0.5, 1): scale by 2^-e (exact) where lq > kSumRescale
+          const int e = (!over && lq > kSumRescale) ? __builtin_amdgcn_frexp_expf(lq) : 0;
+          const float alpha = __builtin_amdgcn_ldexpf(1.f, -e);
           l_run[j] *= alpha;
-          // Each accumulator block goes out of the accumulation registers and
-          // back through this lane's own 16 bytes of LDS, so the compiler
-          // never holds the output blocks anywhere but in those registers.
-#pragma unroll
-          for (int b = 0; b < DB; ++b) {
-            f32x4 x;
-            asm volatile("ds_write_b128 %1, %2\n\ts_waitcnt lgkmcnt(0)\n\tds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
-                         : "=&v"(x)
-                         : "v"(rsc_lane), "a"(oacc[b][j])
-                         : "memory");
-            x = x * alpha;
-            asm volatile("ds_write_b128 %1, %2\n\ts_waitcnt lgkmcnt(0)\n\tds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
-                         : "=&a"(oacc[b][j])
-                         : "v"(rsc_lane), "v"(x)
-                         : "memory");
-          }
-          m_run[j] = m_new;
+          scale_out(j, alpha);
+          m_run[j] += (float)e;
         }
       }
     }
   };
 
-  auto step = [&](int t, f32x4* sc, f32x4* sn, bf16* kc, bf16* kn, bf16* vc, bf16* vn) {
-    const int k0 = t * kBC;
+  // The whole key loop of this workgroup; EXACT as above.  Returns (the same
+  // in every wave) whether the sum check found a row it cannot bound.
+  auto run = [&](auto exact_c) {
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int j = 0; j < QB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[b][j][r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      m_run[j] = kNegInf;
+      l_run[j] = 0.f;
+    }
+    if (ntiles > 0) issue_k(kbuf0, 0);
+    if (ntiles > 1) issue_k(kbuf1, 1);
+    if (ntiles > 0) issue_v(vbuf0, 0);
     wait_vm_all();
-    __syncthreads();  // K(t+1) and V(t) resident for every wave; tile t-1 fully consumed
-    if (k0 + kBC > Nk) {  // tail tile: V rows past the last key must read as zero
-      const int first = Nk - k0;
-      for (int idx = tid; idx < (kBC - first) * CPR; idx += THREADS) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(vc + (first + idx / CPR) * D + (idx % CPR) * 8) = z;
+    __syncthreads();
+    f32x4 sa[KB * QB], sb[KB * QB];
+    if (wnt > 0) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbuf0 + koff(kb, kk));
+#pragma unroll
+          for (int j = 0; j < QB; ++j) {
+            if (kk == 0)
+              mfma16_s0(sa[4 * kb + j], a, qreg[j][kk]);
+            else
+              mfma16_s(sa[4 * kb + j], a, qreg[j][kk]);
+          }
+        }
+      mfma_drain();
+      mask(0, sa);
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sa[4 * kb + j][r]);
+        // a query with no visible key keeps a finite reference (its p are all 0)
+        const float m0 = quad_max(mx);
+        m_run[j] = m0 == kNegInf ? 0.f : m0 * scale_log2;
       }
-      __syncthreads();
     }
-    if (t >= wnt) {  // nothing to compute here, but this wave's share of the loads still goes out
-      if (t + 2 < ntiles) issue_k(kc, t + 2);
-      if (t + 1 < ntiles) issue_v(vn, t + 1);
-      return;
+
+    bool bad = false;
+    auto step = [&](int t, f32x4* sc, f32x4* sn, bf16* kc, bf16* kn, bf16* vc, bf16* vn) {
+      const int k0 = t * kBC;
+      wait_vm_all();
+      __syncthreads();  // K(t+1) and V(t) resident for every wave; tile t-1 fully consumed
+      if (k0 + kBC > Nk) {  // tail tile: V rows past the last key must read as zero
+        const int first = Nk - k0;
+        for (int idx = tid; idx < (kBC - first) * CPR; idx += THREADS) {
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(vc + (first + idx / CPR) * D + (idx % CPR) * 8) = z;
+        }
+        __syncthreads();
+      }
+      if (t >= wnt) {  // nothing to compute here, but this wave's share of the loads still goes out
+        if (t + 2 < ntiles) issue_k(kc, t + 2);
+        if (t + 1 < ntiles) issue_v(vn, t + 1);
+        return;
+      }
+      const int k0n = k0 + kBC;
+      tile_slots(exact_c, (CAUSAL && k0n + kBC - 1 > qw + off) || (k0n + kBC > Nk), t, sc, sn, kn, vc, kc, vn, bad);
+    };
+
+    for (int t = 0; t < ntiles; t += 2) {  // unrolled by two so S(t) and S(t+1) swap registers
+      step(t, sa, sb, kbuf0, kbuf1, vbuf0, vbuf1);
+      if (t + 1 < ntiles) step(t + 1, sb, sa, kbuf1, kbuf0, vbuf1, vbuf0);
     }
-    const int k0n = k0 + kBC;
-    tile_slots((CAUSAL && k0n + kBC - 1 > qw + off) || (k0n + kBC > Nk), t, sc, sn, kn, vc, kc, vn);
+    mfma_drain();
+    // also the barrier after which the ring may be loaded again
+    return __syncthreads_or(bad ? 1 : 0) != 0;
   };
 
-  for (int t = 0; t < ntiles; t += 2) {  // unrolled by two so S(t) and S(t+1) swap registers
-    step(t, sa, sb, kbuf0, kbuf1, vbuf0, vbuf1);
-    if (t + 1 < ntiles) step(t + 1, sb, sa, kbuf1, kbuf0, vbuf1, vbuf0);
-  }
-  mfma_drain();
+  if (run(std::false_type{})) run(std::true_type{});
 
 #pragma unroll
   for (int j = 0; j < QB; ++j) {

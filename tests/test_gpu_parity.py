@@ -133,6 +133,30 @@ def test_drifting_scores_forward(N, causal, d):
     _fwd_compare(f"drift N={N} d={d} causal={causal}", q, k, v, causal, 1 / math.sqrt(d))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("drift", [12.0, 40.0])
+def test_steep_scores_forward(drift, causal):
+    """Scores that climb by about 40 (drift 12) or 130 (drift 40) powers of
+    two per 64-key tile: far past what the d = 128 forward bounds with its
+    row-sum check, so its workgroups must fall back to the exact running max
+    (with drift 40, 2^(s - m) against an earlier tile's reference is not even
+    finite in fp32)."""
+    q, k, v = workloads.drifting_inputs(1, 2, 300, 128, drift=drift, seed=int(drift))
+    _fwd_compare(f"steep drift={drift} causal={causal}", q, k, v, causal, 1 / math.sqrt(128))
+
+
+@pytest.mark.parametrize("height", [3.0, 8.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_spiked_keys_forward(causal, height):
+    """A band of keys (700..719 of 1000) scoring about height·128 above the
+    rest: with height 3 a one-tile jump of ~50 powers of two, with height 8
+    ~130.  Causal rows before the band never see it, the others do, so some
+    workgroups of one launch keep the row-sum check and others fall back."""
+    for d in (64, 128):
+        q, k, v = workloads.spiked_inputs(1, 2, 1000, d, 700, 720, height=height, seed=int(height) + d)
+        _fwd_compare(f"spike d={d} height={height} causal={causal}", q, k, v, causal, 1 / math.sqrt(d))
+
+
 def test_forward_is_deterministic_and_n0_is_noop():
     q, k, v = cuda(*workloads.attention_inputs(1, 8, 2000, 128, "bf16", seed=5))
     a = fa().forward(q, k, v, causal=True)

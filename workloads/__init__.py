@@ -108,6 +108,25 @@ def drifting_inputs(B, H, N, d, drift=4.0, seed=0):
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
+def spiked_inputs(B, H, N, d, lo, hi, height=8.0, seed=0):
+    """Q, K, V bf16 [B, H, N, d] where only keys lo..hi-1 score far above the rest.
+
+    Queries and keys are N(0, 1); every query gets sqrt(d)·u along one random
+    unit direction u and the keys lo..hi-1 get height·sqrt(d)·u, so their
+    scores exceed the others' by about height·d.  Rows that see those keys
+    meet, within one tile, a maximum far above every earlier key; rows that
+    do not (causal rows before lo) never do.
+    """
+    g = _gen(seed)
+    u = torch.randn(d, generator=g, dtype=torch.float32)
+    u = u / u.norm()
+    q = torch.randn(B, H, N, d, generator=g, dtype=torch.float32) + math.sqrt(d) * u
+    k = torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
+    v = torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
+    k[:, :, lo:hi] += height * math.sqrt(d) * u
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
 @dataclass
 class PagedInputs:
     q: torch.Tensor            # [S, H, d] bf16
