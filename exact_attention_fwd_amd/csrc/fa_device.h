@@ -323,25 +323,6 @@ __device__ __forceinline__ void mfma16_s_here(f32x4& s, const bf16x8& a, const b
 __device__ __forceinline__ void mfma16_o_here(f32x4& o, const bf16x8& a, const bf16x8& p) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(p));
 }
-// Softmax operations for software pipelines laid out by hand (the w64
-// forward), each one instruction that stays where it is written (between
-// the products of its pipeline slot).  The callers place every consumer of
-// a result at least one slot (one product) after its producer, so no result
-// is read by the next instruction and no wait states are needed.
-// d = a·b − c (c negated by the instruction's source modifier).
-__device__ __forceinline__ void fms_here(float& d, float a, float b, float c) {
-  asm volatile("v_fma_f32 %0, %1, %2, -%3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
-}
-__device__ __forceinline__ void exp2_here(float& d, float a) { asm volatile("v_exp_f32 %0, %1" : "=v"(d) : "v"(a)); }
-__device__ __forceinline__ void add_here(float& d, float a, float b) {
-  asm volatile("v_add_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void accumulate_here(float& d, float a) { asm volatile("v_add_f32 %0, %0, %1" : "+v"(d) : "v"(a)); }
-// lo, hi rounded to bf16 (nearest even) and packed, as pack_bf16x2
-__device__ __forceinline__ void pack_here(uint32_t& d, float lo, float hi) {
-  asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(d) : "v"(lo), "v"(hi));
-}
-
 // More wait states than a 32x32x16 or 16x16x32 product needs before its result is read.
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 

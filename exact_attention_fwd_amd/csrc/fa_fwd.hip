@@ -52,6 +52,15 @@ template <int SPAN>
 constexpr int fma_slot(int x) {
   return (x * SPAN) / 64;
 }
+// The value whose fma is in slot s (at most one: SPAN >= 64 makes fma_slot
+// strictly increasing), or -1.
+template <int SPAN>
+constexpr int value_at_slot(int s) {
+  static_assert(SPAN >= 64, "one fma per slot at most");
+  for (int x = 0; x < 64; ++x)
+    if (fma_slot<SPAN>(x) == s) return x;
+  return -1;
+}
 
 // Rescale the output only when the running max grows by more than this many
 // powers of two.  Between rescales p = 2^(s·scale·log2e − m) <= 2^8: the
@@ -779,25 +788,39 @@ __global__ __launch_bounds__(256, 1) void fwd_w64_kernel(const bf16* __restrict_
         mfma16_o_here(oacc[db][j], op[n % (LOOK + 1)], __builtin_bit_cast(bf16x8, pw[j][c]));
       }
       // score pairs: pi = 16c + 4jp + 2h + w (key chunk c, query block jp, key block 2c + h, registers 2w, 2w+1)
-      static_for<0, 32>([&](auto pic) __attribute__((always_inline)) {
-        constexpr int pi = decltype(pic)::value;
+      // Softmax work of this slot, at most one operation of each kind (the
+      // fma slots of the 64 values are distinct): the fma of value xf, the
+      // exp of value xe (its fma was in the previous slot), the pack and pair
+      // sum of the pair whose second fma was two slots back, and the row sum
+      // of the pair one slot older.  These are plain operations, not asm
+      // statements: the compiler sees what they are and pads only the waits
+      // the hardware needs.  As asm statements they cost a wait state before
+      // nearly every one of them (the compiler counts an asm statement as no
+      // wait at all and treats its result as possibly that of a
+      // transcendental).  The compiler keeps the fma, exp and sums within a
+      // slot or two of where they are written here and issues the packs in
+      // groups of four, well ahead of their products (measured slightly
+      // faster than packs pinned one per slot).
+      constexpr int xf = value_at_slot<PSPAN>(s), xe = value_at_slot<PSPAN>(s - 1);
+      constexpr int xp = value_at_slot<PSPAN>(s - 2), xa = value_at_slot<PSPAN>(s - 3);
+      // value x: pair pi = x / 2 = 16c + 4jp + 2h + w (key chunk c, query block
+      // jp, key block 2c + h, registers 2w, 2w+1), register x % 2 of the pair
+      auto score = [&](auto xc) -> float {
+        constexpr int x = decltype(xc)::value, pi = x / 2;
         constexpr int c = pi / 16, jp = (pi / 4) % 4, h = (pi / 2) % 2, w = pi % 2;
-        constexpr int blk = 4 * (2 * c + h) + jp, r = 2 * w;
-        constexpr int f0 = fma_slot<PSPAN>(2 * pi), f1 = fma_slot<PSPAN>(2 * pi + 1), pk = f1 + 2;
-        static_assert(pk <= 64 + 32 * c + jp - 2, "a Pᵀ operand must be packed two slots before its product");
-        static_assert(pk + 1 < DEC, "the row sums are complete before their test");
-        if constexpr (f0 == s) fms_here(px[pi][0], sc[blk][r], scale_log2, m_run[jp]);
-        if constexpr (f1 == s) fms_here(px[pi][1], sc[blk][r + 1], scale_log2, m_run[jp]);
-        if constexpr (f0 + 1 == s) exp2_here(px[pi][0], px[pi][0]);
-        if constexpr (f1 + 1 == s) exp2_here(px[pi][1], px[pi][1]);
-        if constexpr (pk == s) {
-          uint32_t packed;
-          pack_here(packed, px[pi][0], px[pi][1]);
-          pw[jp][c][2 * h + w] = packed;
-          add_here(pt[pi], px[pi][0], px[pi][1]);
-        }
-        if constexpr (pk + 1 == s) accumulate_here(l_run[jp], pt[pi]);  // fp32 sum of the unrounded p
-      });
+        return sc[4 * (2 * c + h) + jp][2 * w + x % 2];
+      };
+      if constexpr (xf >= 0)
+        px[xf / 2][xf % 2] = __builtin_fmaf(score(std::integral_constant<int, xf>{}), scale_log2, -m_run[(xf / 8) % 4]);
+      if constexpr (xe >= 0) px[xe / 2][xe % 2] = exp2_fast(px[xe / 2][xe % 2]);
+      if constexpr (xp >= 0 && xp % 2 == 1) {
+        constexpr int pi = xp / 2, c = pi / 16, jp = (pi / 4) % 4, h = (pi / 2) % 2, w = pi % 2;
+        static_assert(s <= 64 + 32 * c + jp - 2, "a Pᵀ operand must be packed two slots before its product");
+        static_assert(s + 1 < DEC, "the row sums are complete before their test");
+        pw[jp][c][2 * h + w] = pack_bf16x2(px[pi][0], px[pi][1]);
+        pt[pi] = px[pi][0] + px[pi][1];
+      }
+      if constexpr (xa >= 0 && xa % 2 == 1) l_run[(xa / 8) % 4] += pt[xa / 2];  // fp32 sum of the unrounded p
       if constexpr (EXACT) {
         // max of S(t+1): value pair v of block (kb, jq) = (v / 8, (v / 2) % 4), registers 2(v % 2)..
         static_for<0, 32>([&](auto vc_) __attribute__((always_inline)) {
