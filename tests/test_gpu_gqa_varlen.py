@@ -184,6 +184,25 @@ def test_varlen_forward_backward(lens, causal, d):
     _varlen_compare(LENS[lens], 4, 2, d, causal, seed=len(LENS[lens]) + d)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_spiked_sequence(causal):
+    """A packed batch where only keys 500..519 of the first sequence score far
+    above the rest (about 130 powers of two, within one key tile): the
+    workgroups of that sequence's rows that see them must take the d = 128
+    forward's exact-max loop, the others not, and every row must still match
+    the oracle."""
+    lens = [700, 300, 900]
+    cu, q, k, v = workloads.varlen_inputs(lens, 4, 2, 128, seed=77)
+    q, k = workloads.add_spike(q, k, list(range(500, 520)), workloads.spike_direction(128, 78))
+    print(f"[varlen spike] lens={lens} causal={causal}", flush=True)
+    cud, qd, kd, vd = cuda(cu, q, k, v)
+    o, lse = fa().forward_varlen(qd, kd, vd, cud, max(lens), causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_forward_varlen(q, k, v, cu, causal=causal, scale=1 / math.sqrt(128))
+    check("varlen spike O", to64(o), ro, BF16_MAX, BF16_MEAN)
+    check("varlen spike LSE", to64(lse), rl, LSE_MAX)
+
+
 def test_varlen_full_size():
     """The packed causal batch the bench times (16 sequences of 527 .. 7723
     tokens, 80 620 rows, H = 32, d = 128, same seed), forward and backward at
@@ -382,6 +401,21 @@ def test_prefill_paged(case, causal, d):
     print(f"[prefill] {case} causal={causal} d={d}", flush=True)
     p = workloads.prefill_inputs(chunks, ctx, H=8, Hkv=2, d=d, seed=len(chunks) + d, poison=True, spare_pages=3)
     _prefill_compare(f"prefill {case}", p, causal)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_paged_spiked_prefix(causal):
+    """Chunked prefill where cached keys 600..619 of the first sequence (in
+    its prefix) score far above the rest: that sequence's workgroups take the
+    d = 128 forward's exact-max loop through the block table, the second
+    sequence's do not."""
+    chunks, ctx = [300, 200], [1000, 700]
+    p = workloads.prefill_inputs(chunks, ctx, H=8, Hkv=2, d=128, seed=91)
+    q, pool = workloads.add_pool_spike(p.q, p.kv_pool, p.block_table, 0, range(600, 620),
+                                       workloads.spike_direction(128, 92))
+    p = workloads.PrefillInputs(q, p.cu_seqlens_q, pool, p.block_table, p.seq_lens_k, p.page_size)
+    print(f"[prefill spike] causal={causal}", flush=True)
+    _prefill_compare("prefill spike", p, causal)
 
 
 def test_prefill_paged_full_size():

@@ -127,6 +127,38 @@ def spiked_inputs(B, H, N, d, lo, hi, height=8.0, seed=0):
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
+def spike_direction(d, seed):
+    """A random unit vector of length d (fp32), from its own seeded generator."""
+    u = torch.randn(d, generator=_gen(seed), dtype=torch.float32)
+    return u / u.norm()
+
+
+def add_spike(q, k, key_rows, u, height=8.0):
+    """bf16 copies of packed Q [rows, H, d] and K [rows, Hkv, d] with sqrt(d)·u
+    added to every query row and height·sqrt(d)·u to the key rows key_rows
+    (indices along the first axis): those keys score about height·d above
+    the others for every query that sees them."""
+    d = q.shape[-1]
+    q2 = q.to(torch.float32) + math.sqrt(d) * u
+    k2 = k.to(torch.float32)
+    k2[key_rows] += height * math.sqrt(d) * u
+    return q2.to(torch.bfloat16), k2.to(torch.bfloat16)
+
+
+def add_pool_spike(q, kv_pool, block_table, seq, positions, u, height=8.0):
+    """As add_spike for a paged cache: sqrt(d)·u on every query row of the
+    packed Q, height·sqrt(d)·u on the keys of sequence `seq` at the given
+    token positions, found through its block table (page = table[seq][t //
+    page], slot t % page).  Returns bf16 copies of Q and the pool."""
+    d = q.shape[-1]
+    page = kv_pool.shape[2]
+    q2 = q.to(torch.float32) + math.sqrt(d) * u
+    pool = kv_pool.to(torch.float32)
+    for t in positions:
+        pool[int(block_table[seq, t // page]), 0, t % page] += height * math.sqrt(d) * u
+    return q2.to(torch.bfloat16), pool.to(torch.bfloat16)
+
+
 @dataclass
 class PagedInputs:
     q: torch.Tensor            # [S, H, d] bf16
