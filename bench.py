@@ -220,6 +220,26 @@ def bench_forward_gqa(steps, warmup, Hkv=8, warm_s=0.0):
             "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def bench_forward_rope(steps, warmup, warm_s=0.0):
+    """The 16K causal forward of c2a's inputs with the rotary embedding of Q
+    and K fused into the kernel (tables for positions 0..N-1, pairs (i, i+d/2)).
+    Throughput counts the attention FLOPs only, as for the other forwards."""
+    import torch
+    import exact_attention_fwd_amd as fa
+    import workloads
+    w = workloads.CONFIGS["c2a"]
+    q, k, v = (t.to("cuda:0") for t in workloads.workload_inputs(w))
+    cos, sin = (t.to("cuda:0") for t in workloads.rope_tables(w.N, w.d))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
+    fn = lambda: fa.forward_rope(q, k, v, cos, sin, causal=True, scale=w.scale, out=o, lse=lse)
+    avg, med, total = timed_launches(fn, steps, warmup, warm_s=warm_s)
+    fl = fwd_flops(w.B, w.H, w.N, w.d, True)
+    return {"workload": "fwd_rope_causal_1x32x16384x128", "kernel": fwd_kernel_name(128, rope=True),
+            "flops_per_launch": fl, "avg_ms": avg, "median_ms": med, "tflops": fl / (avg * 1e-3) / 1e12,
+            "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def bench_varlen(steps, warmup, backward=False, warm_s=0.0):
     """Packed variable-length causal forward (or backward), H=32, d=128."""
     import torch
@@ -397,7 +417,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["fwd", "fwd32k", "fwdnc", "fwd4k", "bwd", "decode", "copy", "fwdgqa",
-                                       "fwdvarlen", "bwdvarlen", "decodegqa", "prefill", "bwdgqa"], default=None,
+                                       "fwdvarlen", "bwdvarlen", "decodegqa", "prefill", "bwdgqa", "fwdrope"], default=None,
                     help="run one path only (for profiler runs); prints its record")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm-s", type=float, default=None, metavar="SECONDS",
@@ -432,7 +452,8 @@ def main():
                "bwdvarlen": lambda: bench_varlen(args.steps, args.warmup, backward=True, warm_s=ws),
                "decodegqa": lambda: bench_decode(args.steps, args.warmup, Hkv=8, warm_s=ws),
                "prefill": lambda: bench_prefill(args.steps, args.warmup, warm_s=ws),
-               "bwdgqa": lambda: bench_backward_gqa(args.steps, args.warmup, warm_s=ws)}[args.only]()
+               "bwdgqa": lambda: bench_backward_gqa(args.steps, args.warmup, warm_s=ws),
+               "fwdrope": lambda: bench_forward_rope(args.steps, args.warmup, warm_s=ws)}[args.only]()
         rec["warm_s"] = ws
         if _POWER["result"] is not None:
             rec["power"] = _POWER["result"]
@@ -453,7 +474,8 @@ def main():
                     ("fwd varlen", lambda: bench_varlen(max(5, args.steps // 2), 2, warm_s=ws)),
                     ("bwd varlen", lambda: bench_varlen(max(5, args.steps // 2), 2, backward=True, warm_s=ws)),
                     ("decode c4 gqa 32q/8kv", lambda: bench_decode(args.steps, args.warmup, Hkv=8, warm_s=ws)),
-                    ("prefill paged", lambda: bench_prefill(max(5, args.steps // 2), 2, warm_s=ws))):
+                    ("prefill paged", lambda: bench_prefill(max(5, args.steps // 2), 2, warm_s=ws)),
+                    ("fwd rope", lambda: bench_forward_rope(max(5, args.steps // 2), 2, warm_s=ws))):
         print(f"# {name}", file=sys.stderr, flush=True)
         secondary.append(dict(f(), warm_s=ws))
         torch.cuda.empty_cache()

@@ -167,6 +167,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 vbuf0[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 vbuf1[TILE];
   __shared__ int ptab[PAGED ? kMaxPrefillPages : 1];  // this sequence's pool pages
+  // Rotary tables of the K tiles in the ring (one object per tile parity, as
+  // the K slots): the cosines, then the sines, of the tile's 64 positions,
+  // loaded with the K tile so that the rotation reads them from LDS.
+  constexpr int RT = (ROPE && !PAGED) ? kTileRows * (D / 2) : 1;
+  __shared__ __attribute__((aligned(1024))) float rtab0[2 * RT];
+  __shared__ __attribute__((aligned(1024))) float rtab1[2 * RT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -241,19 +247,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     }
   }
   // Rotary embedding of a resident K tile (rows k0.., positions k0 + r), in
-  // place in LDS: once per workgroup and tile, every thread one item.
-  auto rope_k = [&](bf16* ks, int k0) {
+  // place in LDS: once per workgroup and tile, every thread one item.  The
+  // tables of the tile's positions are already in LDS (tab: cosines, then
+  // sines; rows past the table read as zero, and so do those K rows).
+  auto rope_k = [&](bf16* ks, const float* tab) {
     if constexpr (ROPE && !PAGED) {
       if (!rope.interleaved) {
         constexpr int PAIRS = CPR / 2;  // chunk c pairs with chunk c + CPR/2
         for (int w = tid; w < kTileRows * PAIRS; w += kThreads) {
           const int r = w / PAIRS, c = w % PAIRS;
-          const int pos = min(k0 + r, rope.rows - 1);
           bf16x8* px = reinterpret_cast<bf16x8*>(ks + r * D + ((c ^ rm_swz<D>(r)) << 3));
           bf16x8* py = reinterpret_cast<bf16x8*>(ks + r * D + (((c + PAIRS) ^ rm_swz<D>(r)) << 3));
           float cs[8], sn[8];
-          load_f32<8>(cs, rope.cos + (size_t)pos * (D / 2) + 8 * c);
-          load_f32<8>(sn, rope.sin + (size_t)pos * (D / 2) + 8 * c);
+          load_f32<8>(cs, tab + r * (D / 2) + 8 * c);
+          load_f32<8>(sn, tab + RT + r * (D / 2) + 8 * c);
           bf16x8 x = *px, y = *py;
           rotate8(x, y, cs, sn);
           *px = x;
@@ -262,11 +269,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       } else {
         for (int w = tid; w < kTileRows * CPR; w += kThreads) {
           const int r = w / CPR, c = w % CPR;
-          const int pos = min(k0 + r, rope.rows - 1);
           bf16x8* px = reinterpret_cast<bf16x8*>(ks + r * D + ((c ^ rm_swz<D>(r)) << 3));
           float cs[4], sn[4];
-          load_f32<4>(cs, rope.cos + (size_t)pos * (D / 2) + 4 * c);
-          load_f32<4>(sn, rope.sin + (size_t)pos * (D / 2) + 4 * c);
+          load_f32<4>(cs, tab + r * (D / 2) + 4 * c);
+          load_f32<4>(sn, tab + RT + r * (D / 2) + 4 * c);
           bf16x8 x = *px;
           rotate8_interleaved(x, cs, sn);
           *px = x;
@@ -308,6 +314,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < DMA_PER_WAVE; ++i)
         lds_dma16(rv, slot + (wave * DMA_PER_WAVE + i) * 512, vdma[i] + (uint32_t)t * (64 * kvs * 2));
+    }
+  };
+
+  // The rotary tables of K tile t into a table slot: 64 table rows of D/2
+  // fp32 each (one contiguous block per table) as 1 KiB direct-to-LDS loads,
+  // lane l writing bytes 16l..16l+15 of its block; rows past the tables'
+  // end read as zero.
+  auto issue_tab = [&](float* tab, int t) {
+    if constexpr (ROPE && !PAGED) {
+      constexpr int BYTES = kTileRows * (D / 2) * 4;
+      constexpr int NB = BYTES / 1024, PER = NB / kWaves;
+      static_assert(PER >= 1 && NB % kWaves == 0, "table blocks split evenly over the wavefronts");
+      const uint32_t tbytes = (uint32_t)max(rope.rows, 0) * (uint32_t)(D / 2) * 4u;
+      const auto rc = make_rsrc(rope.cos, tbytes), rs = make_rsrc(rope.sin, tbytes);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int blk = wave * PER + i;
+        const uint32_t off = (uint32_t)t * (uint32_t)BYTES + (uint32_t)blk * 1024u + 16u * (uint32_t)lane;
+        lds_dma16(rc, tab + blk * 256, off);
+        lds_dma16(rs, tab + RT + blk * 256, off);
+      }
     }
   };
 
@@ -371,11 +398,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int wnt = (qw >= N) ? 0 : (CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / kBC + 1)) : ntiles);
 
   if (ntiles > 0) issue_k(kbuf0, 0);
+  if (ntiles > 0) issue_tab(rtab0, 0);
   if (ntiles > 1) issue_k(kbuf1, 1);
+  if (ntiles > 1) issue_tab(rtab1, 1);
   if (ntiles > 0) issue_v(vbuf0, 0);
   wait_vm_all();
   __syncthreads();
-  if (ntiles > 0) rope_k(kbuf0, 0);
+  if (ntiles > 0) rope_k(kbuf0, rtab0);
   f32x16 sa[2], sb[2];
   if (wnt > 0) {
     scores(kbuf0, sa);
@@ -476,11 +505,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   };
 
   // kc / vc: the slots of tile t (parity of t); kn / vn: the other ones.
-  auto step = [&](int t, f32x16* sc, f32x16* sn, bf16* kc, bf16* kn, bf16* vc, bf16* vn) {
+  auto step = [&](int t, f32x16* sc, f32x16* sn, bf16* kc, bf16* kn, bf16* vc, bf16* vn, float* tc, float* tn) {
     const int k0 = t * kBC;
     wait_vm_all();
     __syncthreads();  // K(t+1) and V(t) resident for every wave; tile t-1 fully consumed
     if (t + 2 < ntiles) issue_k(kc, t + 2);
+    if (t + 2 < ntiles) issue_tab(tc, t + 2);
     if (t + 1 < ntiles) issue_v(vn, t + 1);
     if (k0 + kBC > Nk) {  // tail tile: V rows past the last key must read as zero, whatever the loads left
       const int first = Nk - k0;
@@ -490,15 +520,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       }
       __syncthreads();
     }
-    if (t + 1 < ntiles) rope_k(kn, (t + 1) * kBC);
+    if (t + 1 < ntiles) rope_k(kn, tn);
     if (t >= wnt) return;
     const int k0n = k0 + kBC;
     tile_slots((CAUSAL && k0n + kBC - 1 > qw + off) || (k0n + kBC > Nk), t, sc, sn, kn, vc);
   };
 
   for (int t = 0; t < ntiles; t += 2) {  // unrolled by two so S(t) and S(t+1) swap registers
-    step(t, sa, sb, kbuf0, kbuf1, vbuf0, vbuf1);
-    if (t + 1 < ntiles) step(t + 1, sb, sa, kbuf1, kbuf0, vbuf1, vbuf0);
+    step(t, sa, sb, kbuf0, kbuf1, vbuf0, vbuf1, rtab0, rtab1);
+    if (t + 1 < ntiles) step(t + 1, sb, sa, kbuf1, kbuf0, vbuf1, vbuf0, rtab1, rtab0);
   }
 
   if (qw >= N || qrow >= N) return;
