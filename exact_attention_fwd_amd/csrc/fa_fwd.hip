@@ -87,38 +87,52 @@ __device__ __forceinline__ uint32_t bf16_rne_f64(double x) {
   return __float_as_uint((float)__longlong_as_double((long long)u)) >> 16;
 }
 
-// Rotation of one feature pair (a, b) by (c, s), rounded to bf16: the exact
-// rotation (a·c − b·s, a·s + b·c) rounded to nearest.  Computed in fp32, whose
-// error is below e = 2^-21·(|a|+|b|)·(|c|+|s|); when the bf16 roundings of
-// r − e and r + e agree, every value in between (the exact one included)
-// rounds the same way.  Otherwise (rare: r within e of a rounding boundary)
-// the lane recomputes the pair in fp64, where the products of bf16 and fp32
-// values are exact and only the sum is rounded, and rounds that directly.
-__device__ __forceinline__ void rotate_pair(float a, float b, float c, float s, uint32_t& ox, uint32_t& oy) {
-  const float xr = __builtin_fmaf(a, c, -(b * s));
-  const float yr = __builtin_fmaf(a, s, b * c);
-  const float e = (__builtin_fabsf(a) + __builtin_fabsf(b)) * (__builtin_fabsf(c) + __builtin_fabsf(s)) * 0x1p-21f;
-  const uint32_t wx = pack_bf16x2(xr - e, xr + e), wy = pack_bf16x2(yr - e, yr + e);
-  ox = pack_bf16x2(xr, xr) & 0xffffu;
-  oy = pack_bf16x2(yr, yr) & 0xffffu;
-  if (((wx ^ (wx >> 16)) | (wy ^ (wy >> 16))) & 0xffffu) {
-    const double ad = a, bd = b, cd = c, sd = s;
-    ox = bf16_rne_f64(ad * cd - bd * sd);
-    oy = bf16_rne_f64(ad * sd + bd * cd);
+// Rotation of feature pairs (a, b) by (c, s), rounded to bf16: the exact
+// rotation (a·c − b·s, a·s + b·c) rounded to nearest.  Computed in fp32,
+// whose error is below e = 2^-21·(|a|+|b|)·(|c|+|s|); when the bf16 roundings
+// of (x − e, y − e) and (x + e, y + e) agree (one packed pair each, compared
+// as one word), every value in between (the exact one included) rounds the
+// same way, and the lower pair is the result.  Otherwise (rare: a value
+// within e of a rounding boundary) the lane recomputes its pairs in fp64,
+// where the products of bf16 and fp32 values are exact and only the sum is
+// rounded, and rounds that directly.  NP pairs at a time; out[j] holds pair
+// j as (x in the low 16 bits, y in the high 16 bits).
+template <int NP>
+__device__ __forceinline__ void rotate_pairs(const float* a, const float* b, const float* c, const float* s,
+                                             uint32_t* out) {
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const float xr = __builtin_fmaf(a[j], c[j], -(b[j] * s[j]));
+    const float yr = __builtin_fmaf(a[j], s[j], b[j] * c[j]);
+    const float e =
+        (__builtin_fabsf(a[j]) + __builtin_fabsf(b[j])) * (__builtin_fabsf(c[j]) + __builtin_fabsf(s[j])) * 0x1p-21f;
+    out[j] = pack_bf16x2(xr - e, yr - e);
+    bad = bad || (out[j] != pack_bf16x2(xr + e, yr + e));
+  }
+  if (bad) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const double ad = a[j], bd = b[j], cd = c[j], sd = s[j];
+      out[j] = bf16_rne_f64(ad * cd - bd * sd) | (bf16_rne_f64(ad * sd + bd * cd) << 16);
+    }
   }
 }
 
 // Rotate the feature pairs (x[j], y[j]) of 8 bf16 values each by the angles
-// whose cosines / sines are c[j], s[j] (rotate_pair per pair).
+// whose cosines / sines are c[j], s[j].
+// Two pairs at a time (one word of x, one of y), which keeps the live
+// registers within the kernel's budget.
 __device__ __forceinline__ void rotate8(bf16x8& x, bf16x8& y, const float* c, const float* s) {
   u32x4 wx, wy;
 #pragma unroll
-  for (int j = 0; j < 8; j += 2) {
-    uint32_t x0, y0, x1, y1;
-    rotate_pair((float)x[j], (float)y[j], c[j], s[j], x0, y0);
-    rotate_pair((float)x[j + 1], (float)y[j + 1], c[j + 1], s[j + 1], x1, y1);
-    wx[j / 2] = x0 | (x1 << 16);
-    wy[j / 2] = y0 | (y1 << 16);
+  for (int k = 0; k < 4; ++k) {
+    const float a[2] = {(float)x[2 * k], (float)x[2 * k + 1]};
+    const float b[2] = {(float)y[2 * k], (float)y[2 * k + 1]};
+    uint32_t r[2];
+    rotate_pairs<2>(a, b, c + 2 * k, s + 2 * k, r);
+    wx[k] = (r[0] & 0xffffu) | (r[1] << 16);
+    wy[k] = (r[0] >> 16) | (r[1] & 0xffff0000u);
   }
   x = __builtin_bit_cast(bf16x8, wx);
   y = __builtin_bit_cast(bf16x8, wy);
@@ -127,10 +141,13 @@ __device__ __forceinline__ void rotate8(bf16x8& x, bf16x8& y, const float* c, co
 __device__ __forceinline__ void rotate8_interleaved(bf16x8& x, const float* c, const float* s) {
   u32x4 w;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t r0, r1;
-    rotate_pair((float)x[2 * j], (float)x[2 * j + 1], c[j], s[j], r0, r1);
-    w[j] = r0 | (r1 << 16);
+  for (int k = 0; k < 2; ++k) {
+    const float a[2] = {(float)x[4 * k], (float)x[4 * k + 2]};
+    const float b[2] = {(float)x[4 * k + 1], (float)x[4 * k + 3]};
+    uint32_t r[2];
+    rotate_pairs<2>(a, b, c + 2 * k, s + 2 * k, r);
+    w[2 * k] = r[0];
+    w[2 * k + 1] = r[1];
   }
   x = __builtin_bit_cast(bf16x8, w);
 }
