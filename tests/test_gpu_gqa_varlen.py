@@ -533,6 +533,34 @@ def test_forward_rope_long_positions():
         check(f"rope 16K head {h} LSE", to64(lse[0, h].cpu())[rows], rl, LSE_MAX)
 
 
+def test_forward_rope_full_size():
+    """The timed RoPE launch: causal [1,32,16384,128] with tables for positions
+    0..16383; two whole heads (first and last) and sampled rows of three more."""
+    w = workloads.CONFIGS["c2a"]
+    q, k, v = workloads.workload_inputs(w)
+    c, s = workloads.rope_tables(w.N, w.d)
+    print("[rope full] 1x32x16384x128 causal", flush=True)
+    o, lse = fa().forward_rope(*cuda(q, k, v, c, s), causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    pos = np.arange(w.N)
+    rng = np.random.default_rng(5)
+    rows = sorted(set([0, 1, 63, 64, 255, 256, 8191, w.N - 129, w.N - 1] + rng.integers(0, w.N, 40).tolist()))
+    got_o, ref_o, got_l, ref_l = [], [], [], []
+    for h in (0, 1, w.H // 2, w.H - 2, w.H - 1):
+        qr = oracle.apply_rope_bf16(q[0, h], pos, c, s)
+        kr = oracle.apply_rope_bf16(k[0, h], pos, c, s)
+        if h in (0, w.H - 1):
+            ro, rl = oracle.attention_forward(qr, kr, v[0, h], causal=True, scale=w.scale)
+            go, gl = to64(o[0, h]), to64(lse[0, h])
+        else:
+            ro, rl = oracle.attention_forward_rows(qr, kr, v[0, h], rows, causal=True, scale=w.scale)
+            go, gl = to64(o[0, h])[rows], to64(lse[0, h])[rows]
+        got_o.append(go.ravel()), ref_o.append(ro.ravel()), got_l.append(gl.ravel()), ref_l.append(rl.ravel())
+    check("rope full O", np.concatenate(got_o), np.concatenate(ref_o), BF16_MAX, BF16_MEAN)
+    check("rope full LSE", np.concatenate(got_l), np.concatenate(ref_l), LSE_MAX)
+
+
 def test_forward_rope_varlen():
     cu, q, k, v = workloads.varlen_inputs([300, 0, 1, 129, 64], 4, 1, 128, seed=41)
     c, s = workloads.rope_tables(300, 128)

@@ -92,7 +92,7 @@ def test_c2_long_forward_full_size(cfg):
     print(f"[{cfg}] generating {w.B}x{w.H}x{w.N}x{w.d}", flush=True)
     q, k, v = workloads.workload_inputs(w)
     BH = w.B * w.H
-    full = [0] if cfg == "c2b" else [0, BH - 1]
+    full = [0, BH - 1]
     rows = {h: _sample_rows(w.N, 17 + h) for h in (1, BH // 2, BH - 2)}
     _fwd_compare(cfg, q, k, v, w.causal, w.scale, heads=full, rows=rows)
 
