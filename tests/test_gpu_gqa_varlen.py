@@ -368,6 +368,27 @@ def test_decode_empty_sequence(Hkv):
     check("decode empty neighbours LSE", to64(lse)[keep], rl[keep], LSE_MAX)
 
 
+@pytest.mark.parametrize("Hkv", [8, 2])
+def test_decode_stale_workspace(Hkv):
+    """A caller's workspace that holds NaN in every word (as left by other
+    work): partials past each sequence's last split are never used."""
+    lens = [1, 255, 700, 2000, 1]
+    p = workloads.paged_inputs(num_seqs=len(lens), H=8, Hkv=Hkv, d=128, max_blocks=12, seed=23, seq_lens=lens,
+                               poison=True, spare_pages=2)
+    p.seq_lens[4] = 0
+    qd, pool, bt, sl = cuda(p.q, p.kv_pool, p.block_table, p.seq_lens)
+    need = fa().decode_workspace_bytes(len(lens), 8, 128, 12)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)  # every fp32 word is a NaN
+    o, lse = fa().decode_paged(qd, pool, bt, sl, workspace=ws)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_paged(p.q, p.kv_pool, p.block_table, p.seq_lens, page_size=p.page_size)
+    assert (o[4] == 0).all() and torch.isneginf(lse[4]).all()
+    keep = [0, 1, 2, 3]
+    assert torch.isfinite(o[keep].float()).all()
+    check(f"decode stale workspace Hkv={Hkv} O", to64(o)[keep], ro[keep], BF16_MAX, BF16_MEAN)
+    check(f"decode stale workspace Hkv={Hkv} LSE", to64(lse)[keep], rl[keep], LSE_MAX)
+
+
 # ------------------------------------------------------ paged chunked prefill
 def _prefill_compare(name, p, causal):
     d = p.q.shape[-1]
